@@ -1,0 +1,426 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference of one sparse Mixture-of-Experts
+ * FFN layer.  TEST INFRASTRUCTURE ONLY: only the test-suite, the smoke check
+ * and the CPU-baseline leg of the benchmark may load it.  It shares no code,
+ * header, table or constant with the GPU library and includes nothing from it.
+ *
+ * What it follows (cited by page title and section):
+ *  - "15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选 8 个":
+ *    sigmoid scores of the router logits, a selection-only bias, groups of
+ *    E/G experts scored by the sum of their two best biased scores, the best
+ *    topk_group groups kept, top-k experts chosen among the kept groups, gates
+ *    = unbiased scores of the chosen experts renormalised and multiplied by the
+ *    routed scaling factor, output = gate-weighted sum of the chosen experts
+ *    plus the shared experts.
+ *  - "MoE架构揭秘：大模型参数激活率与专家路由机制解析", section 3.1: router =
+ *    linear layer to E logits, softmax, top-k.
+ *  - "GPT-4 Has 1.8 Trillion Parameters. It Uses 2% of Them Per Token",
+ *    section 2.2 (expert capacity): an expert accepts at most C tokens; tokens
+ *    beyond it go to their next-best expert; its MoEBlock sketch takes the
+ *    softmax over the top-k logits, i.e. renormalised softmax gates.
+ *  - same DeepSeek page, section "671B 和 37B 的参数账": an expert is three
+ *    H x I matrices (gate, up, down); the router is E x H.
+ *  - "MoE on KnightLi的博客", activation-function section: SwiGLU expert FFN.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - ties in every ranking are broken by the lower index;
+ *  - softmax routing selects on the fp32 logits (softmax is monotone);
+ *  - selection always works on fp32 values; sigmoid selection uses the fp32
+ *    sigmoid defined below (sigmoid32) so that it is reproducible bit for bit;
+ *  - capacity C = ceil(((cf*T)*k)/E) in IEEE double, tokens served first come
+ *    first served in index order, each taking its best-ranked allowed experts
+ *    that still have room; slots left empty get index -1 and gate 0; groups
+ *    are not re-chosen after overflow; gates are computed on the final set;
+ *  - shared expert s for token t lives at row T*k + s*T + t of the row space.
+ *
+ * Arithmetic: every dot product, activation, gate and sum is evaluated in
+ * double from the exact input values; the router logits are rounded once to
+ * fp32 because selection is defined on fp32 logits.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int32_t H, E, S, k, G, topk_group, I;
+  int32_t scoring;          /* 0 = softmax, 1 = sigmoid                       */
+  int32_t renorm;           /* 1 = renormalise the selected gates             */
+  double scale;             /* routed scaling factor                          */
+  double capacity_factor;   /* <= 0 : no capacity limit                       */
+  int32_t dtype;            /* 0 = fp32 inputs, 1 = bf16 inputs (bit patterns) */
+} oracle_layer;
+
+/* ---- input access --------------------------------------------------------- */
+
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* element i of a row-major array of fp32 (dtype 0) or bf16 bits (dtype 1) */
+static double elem(const void* base, int dtype, int64_t i) {
+  if (dtype == 1) return bf16_to_double(((const uint16_t*)base)[i]);
+  return (double)((const float*)base)[i];
+}
+
+/* ---- fp32 sigmoid used for selection -------------------------------------- */
+/* exp32(z) for z <= 0: Cody-Waite reduction z = n*ln2 + r with n = rint(z*log2e)
+ * and ln2 split in a high and a low part, e^r by the degree-7 Taylor polynomial
+ * (coefficients 1/j! rounded to fp32) in Horner form with fused multiply-adds,
+ * and a final exact scaling by 2^n.  Every step is one correctly rounded IEEE
+ * fp32 operation, so the result is fixed bit for bit by this description. */
+static const float EXP32_LOG2E = 0x1.715476p+0f;
+static const float EXP32_LN2_HI = 0x1.62e4p-1f;
+static const float EXP32_LN2_LO = 0x1.7f7d1cp-20f;
+static const float EXP32_C[8] = {0x1p+0f,       0x1p+0f,       0x1p-1f,       0x1.555556p-3f,
+                                 0x1.555556p-5f, 0x1.111112p-7f, 0x1.6c16c2p-10f, 0x1.a01a02p-13f};
+
+float oracle_exp32(float z) {
+  float t = z * EXP32_LOG2E;
+  float n = rintf(t);
+  float r = fmaf(-n, EXP32_LN2_HI, z);
+  r = fmaf(-n, EXP32_LN2_LO, r);
+  float p = EXP32_C[7];
+  for (int j = 6; j >= 0; --j) p = fmaf(p, r, EXP32_C[j]);
+  return ldexpf(p, (int)n);
+}
+
+/* sigmoid32(l): clamp l to [-80, 80]; for l >= 0, 1/(1 + exp32(-l)); for
+ * l < 0, e/(1 + e) with e = exp32(l).  The clamp keeps every intermediate a
+ * normal fp32 number. */
+float oracle_sigmoid32(float l) {
+  if (l > 80.0f) l = 80.0f;
+  if (l < -80.0f) l = -80.0f;
+  if (l >= 0.0f) {
+    float e = oracle_exp32(-l);
+    float d = 1.0f + e;
+    return 1.0f / d;
+  } else {
+    float e = oracle_exp32(l);
+    float d = 1.0f + e;
+    return e / d;
+  }
+}
+
+void oracle_sigmoid32_array(int64_t n, const float* in, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_sigmoid32(in[i]);
+}
+
+void oracle_exp32_array(int64_t n, const float* in, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_exp32(in[i]);
+}
+
+/* ---- router logits -------------------------------------------------------- */
+/* logits[t,e] = fl32( sum_h x[t,h] * w_router[e,h] + logit_bias[e] ) */
+int oracle_router_logits(const oracle_layer* L, int64_t T, const void* x, const void* w_router,
+                         const float* logit_bias, float* logits) {
+  const int64_t H = L->H, E = L->E;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t h = 0; h < H; ++h) acc += elem(x, L->dtype, t * H + h) * elem(w_router, L->dtype, e * H + h);
+      if (logit_bias) acc += (double)logit_bias[e];
+      logits[t * E + e] = (float)acc;
+    }
+  }
+  return 0;
+}
+
+/* ---- selection ------------------------------------------------------------ */
+
+/* a ranks before b: higher value first, lower index on equal values */
+static int ranks_before(float va, int ia, float vb, int ib) { return va > vb || (va == vb && ia < ib); }
+
+/* Sort ids[0..n) by (value desc, index asc).  Plain insertion sort: n <= a few
+ * hundred and it keeps the code free of shared state. */
+static void rank_sort(int* ids, int n, const float* v) {
+  for (int i = 1; i < n; ++i) {
+    int cur = ids[i], j = i - 1;
+    while (j >= 0 && ranks_before(v[cur], cur, v[ids[j]], ids[j])) {
+      ids[j + 1] = ids[j];
+      --j;
+    }
+    ids[j + 1] = cur;
+  }
+}
+
+static double sigmoid64(double l) { return 1.0 / (1.0 + exp(-l)); }
+
+/* Per token: the selection score of each expert (fp32), the allowed set after
+ * group limiting, the allowed experts in rank order, and the selection margin.
+ * Returns the number of allowed experts written to `order`. */
+static int token_ranking(const oracle_layer* L, const float* logit, const float* sel_bias, float* score,
+                         int* order, double* margin) {
+  const int E = L->E, G = L->G;
+  for (int e = 0; e < E; ++e) {
+    if (L->scoring == 1) {
+      float s = oracle_sigmoid32(logit[e]);
+      float b = sel_bias ? sel_bias[e] : 0.0f;
+      score[e] = s + b; /* fp32 addition */
+    } else {
+      score[e] = logit[e];
+    }
+  }
+  double m = INFINITY;
+  int n_allowed = 0;
+  if (G > 1) {
+    const int gsz = E / G;
+    float gscore[1024];
+    int gid[1024];
+    for (int g = 0; g < G; ++g) {
+      /* best and second best biased score of the group; an equal value at a
+       * second index counts as the second best */
+      int best = g * gsz;
+      for (int e = g * gsz + 1; e < (g + 1) * gsz; ++e)
+        if (ranks_before(score[e], e, score[best], best)) best = e;
+      int second = -1;
+      for (int e = g * gsz; e < (g + 1) * gsz; ++e) {
+        if (e == best) continue;
+        if (second < 0 || ranks_before(score[e], e, score[second], second)) second = e;
+      }
+      gscore[g] = score[best] + score[second]; /* fp32 addition */
+      gid[g] = g;
+    }
+    rank_sort(gid, G, gscore);
+    if (L->topk_group < G) m = (double)gscore[gid[L->topk_group - 1]] - (double)gscore[gid[L->topk_group]];
+    int kept[1024];
+    memset(kept, 0, sizeof(int) * (size_t)G);
+    for (int i = 0; i < L->topk_group; ++i) kept[gid[i]] = 1;
+    for (int e = 0; e < E; ++e)
+      if (kept[e / gsz]) order[n_allowed++] = e;
+  } else {
+    for (int e = 0; e < E; ++e) order[n_allowed++] = e;
+  }
+  rank_sort(order, n_allowed, score);
+  if (n_allowed > L->k) {
+    double d = (double)score[order[L->k - 1]] - (double)score[order[L->k]];
+    if (d < m) m = d;
+  }
+  if (margin) *margin = m;
+  return n_allowed;
+}
+
+/* Gates of one token over its final selection idx[0..k) (-1 = empty slot). */
+static void token_gates(const oracle_layer* L, const float* logit, const int32_t* idx, double* w) {
+  const int k = L->k, E = L->E;
+  if (L->scoring == 1) {
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j)
+      if (idx[j] >= 0) sum += sigmoid64((double)logit[idx[j]]);
+    for (int j = 0; j < k; ++j) {
+      if (idx[j] < 0) {
+        w[j] = 0.0;
+        continue;
+      }
+      double s = sigmoid64((double)logit[idx[j]]);
+      w[j] = (L->renorm ? s / sum : s) * L->scale;
+    }
+  } else {
+    /* softmax over all E logits; renormalised over the selected experts when
+     * asked (equal to a softmax over the selected logits only) */
+    double mx = -INFINITY;
+    for (int e = 0; e < E; ++e)
+      if ((double)logit[e] > mx) mx = (double)logit[e];
+    double z_all = 0.0, z_sel = 0.0;
+    for (int e = 0; e < E; ++e) z_all += exp((double)logit[e] - mx);
+    for (int j = 0; j < k; ++j)
+      if (idx[j] >= 0) z_sel += exp((double)logit[idx[j]] - mx);
+    for (int j = 0; j < k; ++j) {
+      if (idx[j] < 0) {
+        w[j] = 0.0;
+        continue;
+      }
+      double p = exp((double)logit[idx[j]] - mx);
+      w[j] = (L->renorm ? p / z_sel : p / z_all) * L->scale;
+    }
+  }
+}
+
+/* Capacity of every expert: ceil(((cf*T)*k)/E) in IEEE double, left to right. */
+int64_t oracle_capacity(const oracle_layer* L, int64_t T) {
+  if (!(L->capacity_factor > 0.0)) return -1;
+  double c = ceil(L->capacity_factor * (double)T * (double)L->k / (double)L->E);
+  return (int64_t)c;
+}
+
+/* Selection of every token: idx[T,k] (rank order, -1 = empty slot), gates w[T,k]
+ * (double) and margin[T] (NULL allowed).  With a capacity limit the tokens are
+ * processed in index order and every token takes the best-ranked allowed
+ * experts whose count is still below C. */
+int oracle_select(const oracle_layer* L, int64_t T, const float* logits, const float* sel_bias, int32_t* idx,
+                  double* w, double* margin, int32_t* counts_out) {
+  const int E = L->E, k = L->k;
+  if (E > 4096 || L->G > 1024) return -1;
+  const int64_t cap = oracle_capacity(L, T);
+  if (cap < 0) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      float score[4096];
+      int order[4096];
+      int n = token_ranking(L, logits + t * E, sel_bias, score, order, margin ? margin + t : NULL);
+      for (int j = 0; j < k; ++j) idx[t * k + j] = j < n ? order[j] : -1;
+      token_gates(L, logits + t * E, idx + t * k, w + t * k);
+    }
+  } else {
+    int64_t* count = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    float* score = (float*)malloc(sizeof(float) * (size_t)E);
+    int* order = (int*)malloc(sizeof(int) * (size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+      int n = token_ranking(L, logits + t * E, sel_bias, score, order, margin ? margin + t : NULL);
+      int got = 0;
+      for (int r = 0; r < n && got < k; ++r) {
+        int e = order[r];
+        if (count[e] < cap) {
+          idx[t * k + got++] = e;
+          count[e] += 1;
+        }
+      }
+      for (int j = got; j < k; ++j) idx[t * k + j] = -1;
+      token_gates(L, logits + t * E, idx + t * k, w + t * k);
+    }
+    free(count);
+    free(score);
+    free(order);
+  }
+  if (counts_out) {
+    memset(counts_out, 0, sizeof(int32_t) * (size_t)E);
+    for (int64_t i = 0; i < T * k; ++i)
+      if (idx[i] >= 0) counts_out[idx[i]] += 1;
+  }
+  return 0;
+}
+
+/* ---- permutation ------------------------------------------------------------ */
+/* Rows of the routed experts ordered by (expert asc, token asc):
+ * counts[e], offsets[0..E] (exclusive prefix sum), row_token[row] = token,
+ * slot_row[t*k+j] = row of (t, slot j) or -1 for an empty slot.  Shared expert
+ * s takes rows T*k + s*T + t, so row_token has T*k + S*T entries (entries
+ * between offsets[E] and T*k are -1). */
+int oracle_permute(const oracle_layer* L, int64_t T, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                   int32_t* row_token, int32_t* slot_row) {
+  const int E = L->E, k = L->k, S = L->S;
+  memset(counts, 0, sizeof(int32_t) * (size_t)E);
+  for (int64_t i = 0; i < T * k; ++i) {
+    if (idx[i] < -1 || idx[i] >= E) return -1;
+    if (idx[i] >= 0) counts[idx[i]] += 1;
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  for (int64_t r = 0; r < T * k + (int64_t)S * T; ++r) row_token[r] = -1;
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int e = 0; e < E; ++e) fill[e] = offsets[e];
+  for (int64_t t = 0; t < T; ++t) {
+    for (int j = 0; j < k; ++j) {
+      int e = idx[t * k + j];
+      if (e < 0) {
+        slot_row[t * k + j] = -1;
+        continue;
+      }
+      int32_t r = fill[e]++;
+      row_token[r] = (int32_t)t;
+      slot_row[t * k + j] = r;
+    }
+  }
+  free(fill);
+  for (int s = 0; s < S; ++s)
+    for (int64_t t = 0; t < T; ++t) row_token[T * k + (int64_t)s * T + t] = (int32_t)t;
+  return 0;
+}
+
+/* ---- experts ---------------------------------------------------------------- */
+/* One SwiGLU expert on one row: y = W_down (silu(W_gate x) * (W_up x)),
+ * silu(g) = g * sigmoid(g); w_gate, w_up are [I,H] and w_down is [H,I]. */
+static void swiglu_row(const oracle_layer* L, const void* x, int64_t x_off, const void* wg, const void* wu,
+                       const void* wd, double* hbuf, double* y) {
+  const int64_t H = L->H, I = L->I;
+  for (int64_t i = 0; i < I; ++i) {
+    double g = 0.0, u = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      double xv = elem(x, L->dtype, x_off + h);
+      g += elem(wg, L->dtype, i * H + h) * xv;
+      u += elem(wu, L->dtype, i * H + h) * xv;
+    }
+    hbuf[i] = g * sigmoid64(g) * u;
+  }
+  for (int64_t n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < I; ++i) acc += elem(wd, L->dtype, n * I + i) * hbuf[i];
+    y[n] = acc;
+  }
+}
+
+/* y[r,:] = expert(x_rows[r,:]) for n rows of one expert. */
+int oracle_expert_rows(const oracle_layer* L, int64_t n, const void* x_rows, const void* wg, const void* wu,
+                       const void* wd, double* y) {
+  const int64_t H = L->H;
+#pragma omp parallel
+  {
+    double* hbuf = (double*)malloc(sizeof(double) * (size_t)L->I);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) swiglu_row(L, x_rows, r * H, wg, wu, wd, hbuf, y + r * H);
+    free(hbuf);
+  }
+  return 0;
+}
+
+/* Layer output of the listed tokens:
+ *   out[i,:] = sum_j w[t,j] * expert_{idx[t,j]}(x[t]) + sum_s shared_s(x[t]),
+ * t = tokens[i], empty slots skipped.  Expert e's matrices are wg[e], wu[e],
+ * wd[e] (pointer arrays of length E+S, shared experts after the routed ones;
+ * entries no listed token needs may be NULL). */
+int oracle_forward_tokens(const oracle_layer* L, int64_t n_tok, const int64_t* tokens, const void* x,
+                          const int32_t* idx, const double* w, const void* const* wg, const void* const* wu,
+                          const void* const* wd, double* out) {
+  const int64_t H = L->H;
+  const int k = L->k, E = L->E, S = L->S;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* hbuf = (double*)malloc(sizeof(double) * (size_t)L->I);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_tok; ++i) {
+      const int64_t t = tokens[i];
+      double* o = out + i * H;
+      for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[t * k + j];
+        if (e < 0) continue;
+        if (!wg[e] || !wu[e] || !wd[e]) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        swiglu_row(L, x, t * H, wg[e], wu[e], wd[e], hbuf, y);
+        for (int64_t n = 0; n < H; ++n) o[n] += w[t * k + j] * y[n];
+      }
+      for (int s = 0; s < S; ++s) {
+        const int e = E + s;
+        if (!wg[e] || !wu[e] || !wd[e]) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        swiglu_row(L, x, t * H, wg[e], wu[e], wd[e], hbuf, y);
+        for (int64_t n = 0; n < H; ++n) o[n] += y[n];
+      }
+    }
+    free(hbuf);
+    free(y);
+  }
+  return bad ? -1 : 0;
+}
+
+/* ---- parameter arithmetic ---------------------------------------------------- */
+/* One MoE layer: router E*H plus (E+S) experts of three H x I matrices. */
+int64_t oracle_moe_layer_params(int64_t H, int64_t E, int64_t S, int64_t I) { return E * H + (E + S) * 3 * H * I; }
+
+/* Parameters one token passes through in a MoE layer: the router, its k
+ * routed experts and the S shared experts. */
+int64_t oracle_moe_active_params(int64_t H, int64_t E, int64_t S, int64_t k, int64_t I) {
+  return E * H + (k + S) * 3 * H * I;
+}

@@ -1,0 +1,90 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle.c (on the CPU, in a temporary
+directory), builds it, and runs the pin tests against that copy: at least one
+pin must fail.  The shipped oracle is untouched.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_ffn as F
+from tests import test_oracle_permute as P
+from tests import test_oracle_selection as S
+from tests import test_oracle_sigmoid as G
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "group score from the best expert twice": ("gscore[g] = score[best] + score[second];",
+                                               "gscore[g] = score[best] + score[best];"),
+    "routed scaling factor dropped": ("w[j] = (L->renorm ? s / sum : s) * L->scale;",
+                                      "w[j] = (L->renorm ? s / sum : s);"),
+    "ties to the higher index": ("return va > vb || (va == vb && ia < ib);",
+                                 "return va > vb || (va == vb && ia > ib);"),
+    "silu applied to the up projection": ("hbuf[i] = g * sigmoid64(g) * u;", "hbuf[i] = u * sigmoid64(u) * g;"),
+    "down projection transposed": ("acc += elem(wd, L->dtype, n * I + i) * hbuf[i];",
+                                   "acc += elem(wd, L->dtype, i * H + n) * hbuf[i];"),
+    "shared expert not added": ("for (int64_t n = 0; n < H; ++n) o[n] += y[n];",
+                                "for (int64_t n = 0; n < H; ++n) o[n] += 0.0 * y[n];"),
+    "capacity off by one": ("if (count[e] < cap) {", "if (count[e] <= cap) {"),
+    "unnormalised softmax over the selection": ("w[j] = (L->renorm ? p / z_sel : p / z_all) * L->scale;",
+                                                "w[j] = (L->renorm ? p / z_sel : p / z_sel) * L->scale;"),
+    "strided groups": ("if (kept[e / gsz]) order[n_allowed++] = e;", "if (kept[e % G]) order[n_allowed++] = e;"),
+    "ln2 low part dropped": ("r = fmaf(-n, EXP32_LN2_LO, r);", "r = r;"),
+    "logit bias ignored": ("if (logit_bias) acc += (double)logit_bias[e];", "(void)logit_bias;"),
+    "gates from the biased score": ("double s = sigmoid64((double)logit[idx[j]]);\n      w[j]",
+                                    "double s = sigmoid64((double)logit[idx[j]]) + 0.01 * j;\n      w[j]"),
+    "group limit keeps one group too many": ("for (int i = 0; i < L->topk_group; ++i) kept[gid[i]] = 1;",
+                                             "for (int i = 0; i <= L->topk_group && i < G; ++i) kept[gid[i]] = 1;"),
+    "permutation in descending token order": ("for (int e = 0; e < E; ++e) fill[e] = offsets[e];\n  for (int64_t t = 0; t < T; ++t) {",
+                                              "for (int e = 0; e < E; ++e) fill[e] = offsets[e];\n  for (int64_t t = T - 1; t >= 0; --t) {"),
+    "expert gate weight ignored": ("for (int64_t n = 0; n < H; ++n) o[n] += w[t * k + j] * y[n];",
+                                   "for (int64_t n = 0; n < H; ++n) o[n] += y[n];"),
+}
+
+PINS = [
+    G.test_exp32_within_2ulp_of_double_exp, G.test_sigmoid32_closed_forms,
+    S.test_group_whose_best_expert_is_global_max_but_pair_sum_loses_is_dropped,
+    S.test_bias_changes_selection_but_not_gates, S.test_sigmoid_gates_closed_form,
+    S.test_softmax_gates_closed_form, S.test_ties_go_to_lower_index, S.test_softmax_gates_match_library_softmax,
+    S.test_v3_gates_sum_to_scaling_factor, S.test_router_logits_are_the_fp32_rounded_matmul_plus_bias,
+    lambda: S.test_capacity_matches_sequential_simulation(8, 1, 1, 2, 1.0, "softmax"),
+    lambda: S.test_selection_matches_exhaustive_enumeration(16, 4, 2, 3, "sigmoid"),
+    P.test_hand_example,
+    F.test_swiglu_closed_form_with_selection_matrices, F.test_single_expert_layer_is_a_dense_swiglu_ffn,
+    F.test_identical_experts_factor_out, F.test_empty_slots_are_skipped_and_bf16_inputs_are_exact,
+]
+
+
+def _first_failing_pin():
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            return pin
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor must match exactly once"
+    path = tmp_path / "oracle_mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-std=gnu11",
+                           "-o", str(lib), str(path), "-lm"])
+    oracle.use_library(str(lib))
+    try:
+        assert _first_failing_pin() is not None, "no pin caught: " + name
+    finally:
+        oracle.use_library(None)
+
+
+def test_unmodified_oracle_passes_every_pin():
+    assert _first_failing_pin() is None

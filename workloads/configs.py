@@ -1,0 +1,81 @@
+"""Layer shapes: the five workloads plus reduced shapes for full-oracle tests."""
+from dataclasses import dataclass, replace
+from typing import Optional
+
+SOFTMAX = "softmax"
+SIGMOID = "sigmoid"
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    name: str
+    T: int                      # tokens in the batch
+    H: int                      # hidden size
+    E: int                      # routed experts
+    S: int                      # shared experts (always active, unweighted)
+    k: int                      # experts chosen per token
+    I: int                      # expert intermediate size (routed and shared)
+    G: int = 1                  # expert groups
+    topk_group: int = 1         # groups kept per token
+    scoring: str = SOFTMAX      # "softmax" | "sigmoid"
+    renorm: bool = True         # renormalise the selected gates
+    scale: float = 1.0          # routed scaling factor applied to the gates
+    capacity_factor: float = 0.0  # <= 0: unlimited
+    dtype: str = "bf16"         # "bf16" | "f32" for x and every weight
+    sel_bias: Optional[float] = None   # selection bias ~ U(-a, a) when set
+    zipf_s: Optional[float] = None     # Zipf exponent of the per-expert logit offset
+    seed: int = 0
+
+    def with_(self, **kw) -> "LayerShape":
+        return replace(self, **kw)
+
+    @property
+    def rows(self) -> int:
+        """Upper bound of expert rows: every (token, slot) plus S*T shared rows."""
+        return self.T * self.k + self.S * self.T
+
+    def flops(self, assigned_slots: Optional[int] = None) -> float:
+        """Algorithmic FLOPs of one layer call: router GEMM + 3 expert GEMMs
+        over assigned (non-dropped) rows and all shared rows."""
+        a = self.T * self.k if assigned_slots is None else assigned_slots
+        return 2.0 * self.T * self.H * self.E + 6.0 * self.H * self.I * (a + self.S * self.T)
+
+
+CONFIGS = {
+    # Tiny Mixtral-style layer in fp32.
+    "tiny_mixtral_fp32": LayerShape("tiny_mixtral_fp32", T=64, H=256, E=8, S=0, k=2, I=512,
+                                    dtype="f32", seed=101),
+    # Mixtral-8x7B-shaped layer.
+    "mixtral_8x7b": LayerShape("mixtral_8x7b", T=4096, H=4096, E=8, S=0, k=2, I=14336, seed=202),
+    # DeepSeek-V2-shaped layer: softmax without renormalisation.
+    "deepseek_v2": LayerShape("deepseek_v2", T=8192, H=5120, E=160, S=2, k=6, I=1536,
+                              renorm=False, seed=303),
+    # DeepSeek-V3-shaped layer, prefill size.
+    "deepseek_v3_prefill": LayerShape("deepseek_v3_prefill", T=16384, H=7168, E=256, S=1, k=8,
+                                      I=2048, G=8, topk_group=4, scoring=SIGMOID, renorm=True,
+                                      scale=2.5, sel_bias=0.05, seed=404),
+    # DeepSeek-V3-shaped layer, decode size, Zipf-skewed load and expert capacity.
+    "deepseek_v3_decode": LayerShape("deepseek_v3_decode", T=128, H=7168, E=256, S=1, k=8,
+                                     I=2048, G=8, topk_group=4, scoring=SIGMOID, renorm=True,
+                                     scale=2.5, sel_bias=0.05, zipf_s=1.1, capacity_factor=1.25,
+                                     seed=505),
+}
+
+# Reduced shapes with the same routing structure, small enough for the full
+# fp64 oracle to finish in seconds while still spanning several GEMM tiles and
+# ragged tails (T not a multiple of any tile height).
+TEST_SHAPES = {
+    "tiny_mixtral_fp32": CONFIGS["tiny_mixtral_fp32"],
+    "mixtral_small": CONFIGS["mixtral_8x7b"].with_(name="mixtral_small", T=389, H=512, I=1024),
+    "v2_small": CONFIGS["deepseek_v2"].with_(name="v2_small", T=301, H=512, I=384),
+    "v3_small": CONFIGS["deepseek_v3_prefill"].with_(name="v3_small", T=517, H=512, I=256),
+    "v3_decode_small": CONFIGS["deepseek_v3_decode"].with_(name="v3_decode_small", H=512, I=256),
+}
+
+
+def get_config(name: str) -> LayerShape:
+    if name in CONFIGS:
+        return CONFIGS[name]
+    if name in TEST_SHAPES:
+        return TEST_SHAPES[name]
+    raise KeyError(name)

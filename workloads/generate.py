@@ -1,0 +1,82 @@
+"""Seeded synthetic inputs of a layer shape.
+
+Distributions: x ~ N(0, 1); every weight ~ N(0, 1/fan_in) (router and gate/up:
+fan_in = H; down: fan_in = I); optional selection bias ~ U(-a, a) in fp32;
+optional Zipf(s) per-expert logit offset.  bf16 tensors are produced by
+rounding fp32 draws to nearest-even (torch's conversion).
+
+The random stream of each tensor is a torch Philox/CPU generator seeded from
+(shape seed, tensor index), and weight tensors are drawn expert by expert, so
+the bytes depend only on (shape, seed, device type).  Both the HIP path and the
+oracle consume the same bytes: tests draw once and hand the same tensors (or
+host copies of them) to both sides.
+"""
+import math
+
+import numpy as np
+import torch
+
+_TENSORS = ("x", "w_router", "sel_bias", "zipf_perm", "w_gate", "w_up", "w_down")
+
+
+def _seed(base: int, name: str) -> int:
+    return (base * 1_000_003 + 7919 * (_TENSORS.index(name) + 1)) & 0x7FFF_FFFF_FFFF
+
+
+def _gen(device, base: int, name: str) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(base, name))
+    return g
+
+
+def _dtype(cfg):
+    return torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+
+def _normal(shape, std, g, device, dtype):
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(dtype)
+
+
+def zipf_logit_offsets(E: int, s: float, seed: int) -> np.ndarray:
+    """Centred log-pmf of a Zipf(s) law over E ranks, ranks assigned to experts
+    by a seeded permutation.  Added to the router logits it skews the load the
+    way the pages describe real traffic (a few experts take most tokens)."""
+    ranks = np.random.Generator(np.random.PCG64(_seed(seed, "zipf_perm"))).permutation(E) + 1
+    j = np.arange(1, E + 1, dtype=np.float64)
+    logp = -s * np.log(ranks.astype(np.float64)) - math.log(np.sum(j ** -s))
+    return (logp - logp.mean()).astype(np.float32)
+
+
+def make_inputs(cfg, device="cpu", seed=None, T=None):
+    """Return a dict of tensors on `device`:
+    x [T,H], w_router [E,H], w_gate/w_up [E+S,I,H], w_down [E+S,H,I] in the
+    layer dtype; sel_bias [E] fp32 or None; logit_bias [E] fp32 or None."""
+    base = cfg.seed if seed is None else seed
+    T = cfg.T if T is None else T
+    dt = _dtype(cfg)
+    H, E, S, I = cfg.H, cfg.E, cfg.S, cfg.I
+    out = {}
+    out["x"] = _normal((T, H), 1.0, _gen(device, base, "x"), device, dt)
+    out["w_router"] = _normal((E, H), 1.0 / math.sqrt(H), _gen(device, base, "w_router"), device, dt)
+    if cfg.sel_bias:
+        g = _gen(device, base, "sel_bias")
+        u = torch.rand((E,), generator=g, device=device, dtype=torch.float32)
+        out["sel_bias"] = (u * (2.0 * cfg.sel_bias) - cfg.sel_bias).contiguous()
+    else:
+        out["sel_bias"] = None
+    if cfg.zipf_s:
+        out["logit_bias"] = torch.from_numpy(zipf_logit_offsets(E, cfg.zipf_s, base)).to(device)
+    else:
+        out["logit_bias"] = None
+    for name, shape, std in (("w_gate", (I, H), 1.0 / math.sqrt(H)),
+                             ("w_up", (I, H), 1.0 / math.sqrt(H)),
+                             ("w_down", (H, I), 1.0 / math.sqrt(I))):
+        w = torch.empty((E + S,) + shape, device=device, dtype=dt)
+        g = _gen(device, base, name)
+        for e in range(E + S):
+            w[e] = _normal(shape, std, g, device, dt)
+        out[name] = w
+    return out
