@@ -1,0 +1,203 @@
+"""Benchmark of the MoE layer on one MI355X.
+
+One step = one moe_forward call (router, capacity when configured, permute,
+gate/up+SwiGLU GEMM, down GEMM, combine) over one batch of seeded synthetic
+inputs already resident in HBM.  Default workload: the DeepSeek-V3-shaped
+prefill layer (16384 tokens, hidden 7168, 256 routed + 1 shared experts,
+top-8 of 8 groups / 4 kept, intermediate 2048, bf16).
+
+Prints one JSON line: tokens/s of the whole job, the roofline of the dominant
+kernel (gate/up + SwiGLU grouped GEMM, bf16 MFMA) timed live with HIP events
+on the launch stream, and the CPU oracle timed on a bounded token sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at DeepSeek-V3 shape; % bf16 MFMA peak / % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_swiglu_deepseek_v3_prefill_traffic.md")
+GEMM_SRC = os.path.join(ROOT, "routing_expert_ffn_amd", "csrc", "gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_sha():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, or
+    None when the summary is missing or was taken on another kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    sha = re.search(r"gemm_source_sha:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != gemm_source_sha():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(shape, inp, target_s):
+    """The fp64 oracle on a bounded sample of the same workload's tokens."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from tests.hostdata import to_oracle
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    log("cpu baseline: copying inputs to the host")
+    x = to_oracle(inp["x"])
+    wr = to_oracle(inp["w_router"])
+    sb = to_oracle(inp["sel_bias"])
+    lb = to_oracle(inp["logit_bias"])
+    wg, wu, wd = to_oracle(inp["w_gate"]), to_oracle(inp["w_up"]), to_oracle(inp["w_down"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    order = rng.permutation(shape.T)
+
+    def run(tokens):
+        t0 = time.perf_counter()
+        logits = oracle.router_logits(shape, x[tokens], wr, lb)
+        idx, w, _, _ = oracle.select(shape, logits, sb)
+        oracle.forward_tokens(shape, np.arange(len(tokens)), x[tokens], idx, w, lambda e: (wg[e], wu[e], wd[e]))
+        return time.perf_counter() - t0
+
+    n1 = max(cores, 4)
+    t1 = run(order[:n1])
+    per_tok = t1 / n1
+    n2 = int(max(0, (target_s - t1) / per_tok))
+    n2 = min(n2, shape.T - n1)
+    t2 = run(order[n1:n1 + n2]) if n2 > 0 else 0.0
+    n = n1 + n2
+    secs = t1 + t2
+    log("cpu baseline: %d tokens in %.1f s on %d threads" % (n, secs, cores))
+    return {"value": n / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d random tokens of the %d-token %s batch: router logits, selection, %d routed + %d shared "
+                      "SwiGLU experts each and the combine, fp64, %.1f s" % (n, shape.T, shape.name, shape.k,
+                                                                          shape.S, secs)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="deepseek_v3_prefill")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import routing_expert_ffn_amd as moe
+    from workloads import CONFIGS, make_inputs
+
+    shape = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs for", shape.name)
+    inp = make_inputs(shape, device=dev)
+    cfg = moe.make_config(shape, out_dtype="bf16")
+    T = shape.T
+    ws = moe.workspace(cfg, T, dev)
+    out = torch.empty((T, shape.H), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((T, shape.k), dtype=torch.int32, device=dev)
+    counts = torch.empty((shape.E,), dtype=torch.int32, device=dev)
+
+    def step():
+        moe.forward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                    logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], out=out, topk_idx=idx,
+                    expert_counts=counts, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    moe.timing_enable(args.steps * 16)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    kern = moe.timing_read()
+    moe.timing_enable(0)
+    log("timed %d steps: %.3f ms/step" % (args.steps, total_ms / args.steps))
+
+    assigned = int((idx >= 0).sum().item())
+    rows = assigned + shape.S * T
+    gateup_flops = 4.0 * shape.H * shape.I * rows
+    down_flops = 2.0 * shape.H * shape.I * rows
+    layer_flops = shape.flops(assigned)
+    ms_step = total_ms / args.steps
+    kernels = {name: ms / n for name, (ms, n) in kern.items()}
+    gu_ms = kernels.get("gateup_swiglu")
+    achieved = gateup_flops / (gu_ms * 1e-3) / 1e12
+    touched = int((counts > 0).sum().item())
+    weight_bytes = (touched + shape.S) * 3 * shape.H * shape.I * (2 if shape.dtype == "bf16" else 4)
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic",
+        "config": {"workload": shape.name, "tokens": T, "hidden": shape.H, "routed_experts": shape.E,
+                   "shared_experts": shape.S, "top_k": shape.k, "groups": shape.G, "groups_kept": shape.topk_group,
+                   "intermediate": shape.I, "scoring": shape.scoring, "capacity_factor": shape.capacity_factor,
+                   "out_dtype": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                     "kernel": "gateup_swiglu", "flops_per_launch": gateup_flops, "ms_per_launch": gu_ms},
+        "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
+        "layer_mfma_frac": layer_flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "layer_weight_gbs": weight_bytes / (ms_step * 1e-3) / 1e9,
+        "layer_hbm_frac": weight_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "kernels_ms": kernels,
+        "assigned_slots": assigned,
+        "touched_experts": touched,
+    }
+    if shape.T <= 1024:
+        # decode-sized: the weight stream is the bound
+        res["roofline"] = {"bound": "hbm", "achieved": res["layer_weight_gbs"], "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": res["layer_hbm_frac"], "traffic": None,
+                           "kernel": "whole layer (weights of touched experts)"}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * moe.h -- C ABI of one sparse Mixture-of-Experts FFN layer on AMD MI355X
+ * (gfx950).  Built as routing_expert_ffn_amd/libmoe.so.
+ *
+ * The layer (cited by page title and section):
+ *   router logits   l = x W_r^T (+ logit_bias)            "MoE架构揭秘：大模型参数激活率与专家路由机制解析", 3.1
+ *   scoring         softmax over E logits                 same section
+ *                   or sigmoid + selection-only bias      "15. DeepSeek：MLA、MoE 与 MTP", "V3 的 MoE：256 个专家怎样选 8 个"
+ *   group limit     groups of E/G experts scored by the sum of their two best
+ *                   biased scores, topk_group groups kept  same DeepSeek section
+ *   top-k + gates   renormalised softmax ("GPT-4 Has 1.8 Trillion Parameters.
+ *                   It Uses 2% of Them Per Token", MoEBlock sketch in 4.1),
+ *                   plain softmax (DeepSeek-V2, no renormalisation), or
+ *                   unbiased sigmoid scores renormalised x routed_scaling_factor
+ *   capacity        an expert takes at most C tokens; later tokens go to their
+ *                   next-best allowed expert ("GPT-4 Has 1.8 Trillion ...", 2.2)
+ *   experts         SwiGLU FFN y = W_down (silu(W_gate x) * W_up x), shared
+ *                   experts always active and added unweighted
+ *                   ("MoE on KnightLi的博客", activation functions; DeepSeek page,
+ *                   "671B 和 37B 的参数账")
+ *   combine         out = sum_j w_j * expert_{idx_j}(x) + sum_s shared_s(x)
+ *
+ * Conventions shared by every call
+ *  - Every pointer argument that names a tensor is a DEVICE pointer on the
+ *    current HIP device, owned by the caller, row-major and densely packed.
+ *    The library allocates no device memory and keeps no device state.
+ *  - "Input dtype" (moe_config.dtype) applies to x and every weight matrix:
+ *    MOE_BF16 (bfloat16) or MOE_F32.  Logits, gates and biases are fp32.
+ *  - Matrices keep their reduction dimension contiguous: w_router [E,H],
+ *    w_gate/w_up [E+S,I,H], w_down [E+S,H,I]; routed experts 0..E-1 first,
+ *    shared experts E..E+S-1 after them.
+ *  - Row space of the experts: routed rows 0..T*k-1 ordered by (expert asc,
+ *    token asc), shared expert s of token t at row T*k + s*T + t.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and never synchronises the host.
+ *  - Workspace: `ws` is a device buffer of at least moe_workspace_size() bytes,
+ *    256-byte aligned, owned by the caller, not used concurrently by two calls.
+ *  - Errors: arguments are validated before anything is enqueued; on failure
+ *    the call returns a negative moe_status, enqueues nothing and records a
+ *    message for moe_last_error().  A failed kernel launch returns
+ *    MOE_ERR_HIP.  Faults inside kernels surface asynchronously (at the
+ *    caller's next synchronisation).  T == 0 is a successful no-op.
+ *  - Routing is reproducible bit for bit: selection works on fp32 values with
+ *    ties broken by the lower index, and sigmoid selection scores use the fp32
+ *    sigmoid built from correctly rounded operations that moe_route documents.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* bad pointer, size or configuration            */
+  MOE_ERR_UNSUPPORTED = -2, /* valid layer this build does not run          */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+  MOE_ERR_HIP = -4          /* a HIP runtime call failed                    */
+} moe_status;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer description: the fields the DeepSeek page reads from a checkpoint's
+ * config (n_routed_experts, n_shared_experts, num_experts_per_tok, n_group,
+ * topk_group, moe_intermediate_size, routed_scaling_factor, scoring
+ * function) plus the capacity factor of the capacity passage. */
+typedef struct moe_config {
+  int32_t hidden_size;           /* H; bf16 needs H % 256 == 0, f32 H % 4 == 0  */
+  int32_t n_routed_experts;      /* E, 1..1024                                    */
+  int32_t n_shared_experts;      /* S >= 0, each shaped like a routed expert     */
+  int32_t top_k;                 /* k, 1..min(E, 32)                              */
+  int32_t n_group;               /* G >= 1, E % G == 0, E/G >= 2 when G > 1      */
+  int32_t topk_group;            /* 1..G, top_k <= topk_group * E / G            */
+  int32_t moe_intermediate_size; /* I; bf16 needs I % 128 == 0, f32 I % 4 == 0  */
+  int32_t scoring;               /* moe_scoring                                   */
+  int32_t norm_topk_prob;        /* 1: gates renormalised over the selection     */
+  float routed_scaling_factor;   /* multiplies every routed gate (2.5 for V3)    */
+  float capacity_factor;         /* <= 0: unlimited; else C = ceil(cf*T*k/E)    */
+  int32_t dtype;                 /* moe_dtype of x and every weight              */
+  int32_t out_dtype;             /* moe_dtype of `out`                            */
+} moe_config;
+
+/* Bytes of workspace every call below needs for this layer and T tokens
+ * (the largest need of any call; one buffer serves them all).
+ * Returns MOE_ERR_INVALID_ARG for an invalid configuration or T < 0. */
+moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
+
+/* Router: logits, scoring, group-limited top-k, gates, optional capacity.
+ *   x            [T,H] input dtype (unused when logits_in is given)
+ *   w_router     [E,H] input dtype (unused when logits_in is given)
+ *   logit_bias   [E] fp32 added to every logit, or NULL
+ *   sel_bias     [E] fp32 selection-only bias (sigmoid scoring), or NULL
+ *   logits_in    [T,E] fp32 logits to route instead of computing them, or NULL
+ *   logits_out   [T,E] fp32 computed logits (bias included), or NULL
+ *   topk_idx     [T,k] int32 out: chosen experts in rank order, -1 = empty slot
+ *   topk_w       [T,k] fp32 out: gates (0 for an empty slot)
+ *   expert_counts[E] int32 out: tokens per expert, or NULL
+ * Selection score: softmax scoring ranks the fp32 logits; sigmoid scoring
+ * ranks c_e = fl32(sigmoid32(l_e) + sel_bias_e), where sigmoid32 clamps l to
+ * [-80,80] and evaluates 1/(1+e) (l >= 0, e = exp32(-l)) or e/(1+e) (l < 0,
+ * e = exp32(l)); exp32(z) = ldexp(p(r), n), n = rint(fl32(z*0x1.715476p+0)),
+ * r = fma(-n, 0x1.7f7d1cp-20, fma(-n, 0x1.62e4p-1, z)), p = Horner with fma of
+ * the fp32 coefficients {1, 1, 0x1p-1, 0x1.555556p-3, 0x1.555556p-5,
+ * 0x1.111112p-7, 0x1.6c16c2p-10, 0x1.a01a02p-13}.  Group score = fl32(best +
+ * second best) of a group's c.  Ties rank the lower index first.
+ * Capacity: tokens in index order each take their best-ranked allowed experts
+ * with fewer than C tokens so far; C = ceil(((cf*T)*k)/E) in double. */
+moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                     const float* logit_bias, const float* sel_bias, const float* logits_in,
+                     float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: expert histogram and stable permutation of (token, slot) pairs.
+ *   topk_idx       [T,k] int32, each row distinct experts in [0,E) or -1
+ *   expert_counts  [E]   int32 out
+ *   expert_offsets [E+1] int32 out: exclusive prefix sum of the counts
+ *   row_token      [T*k + S*T] int32 out: token of every row (-1 = unused row)
+ *   slot_row       [T,k] int32 out: row of (t, j), -1 for an empty slot
+ * Rows of one expert are in ascending token order.  Out-of-range indices are
+ * the caller's contract violation: they are counted nowhere (undefined rows). */
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Experts: for every routed row r (expert e, token t = row_token[r]) and every
+ * shared row, y_rows[r] = W_down[e] (silu(W_gate[e] x_t) * W_up[e] x_t).
+ *   x              [T,H] input dtype
+ *   w_gate, w_up   [E+S,I,H] input dtype;  w_down [E+S,H,I] input dtype
+ *   expert_offsets [E+1], row_token [T*k+S*T] as written by moe_permute
+ *   y_rows         [T*k+S*T, H] out, input dtype (bf16 rows for bf16 layers);
+ *                  unused routed rows are left untouched
+ * bf16 layers accumulate in fp32 on the matrix cores and round the SwiGLU
+ * activation and y to bf16. */
+moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const void* w_gate,
+                          const void* w_up, const void* w_down, const int32_t* expert_offsets,
+                          const int32_t* row_token, void* y_rows, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine: out[t] = sum_j topk_w[t,j] * y_rows[slot_row[t,j]] (empty slots
+ * skipped) + sum_s y_rows[T*k + s*T + t], accumulated in fp32 in that order.
+ *   y_rows [T*k+S*T, H] input dtype; slot_row, topk_w [T,k]; out [T,H] out_dtype */
+moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, const int32_t* slot_row,
+                       const float* topk_w, void* out, void* stream);
+
+/* The whole layer in one call: route, permute, experts and combine.
+ * out [T,H] in cfg->out_dtype.  topk_idx, topk_w, expert_counts and
+ * logits_out are optional outputs (NULL = keep them in the workspace). */
+moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                       const float* logit_bias, const float* sel_bias, const void* w_gate, const void* w_up,
+                       const void* w_down, void* out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                       float* logits_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+/* Optional per-kernel timing.  moe_timing_enable(n) makes the library bracket
+ * each of its next n kernel launches with hipEventRecord on the launch stream
+ * (n <= 0 disables).  moe_timing_read waits for those events and returns, per
+ * kernel id (< n_kernels), the summed duration in milliseconds and the launch
+ * count; then clears the record.  moe_kernel_name(id) names kernel id (NULL
+ * past the last).  Not thread-safe: time from one thread. */
+moe_status moe_timing_enable(int32_t max_launches);
+moe_status moe_timing_read(double* ms, int64_t* launches, int32_t n_kernels);
+const char* moe_kernel_name(int32_t id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -74,6 +74,7 @@ def _load():
         lib.oracle_permute.argtypes = [P, I64, P, P, P, P, P]
         lib.oracle_expert_rows.argtypes = [P, I64, P, P, P, P, P]
         lib.oracle_forward_tokens.argtypes = [P, I64, P, P, P, P, P, P, P, P]
+        lib.oracle_combine.argtypes = [P, I64, P, P, P, P]
         lib.oracle_moe_layer_params.restype = I64
         lib.oracle_moe_layer_params.argtypes = [I64, I64, I64, I64]
         lib.oracle_moe_active_params.restype = I64
@@ -219,6 +220,20 @@ def forward(cfg, x, w_router, w_gate, w_up, w_down, sel_bias=None, logit_bias=No
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     out = forward_tokens(cfg, tokens, x, idx, w, lambda e: (w_gate[e], w_up[e], w_down[e]))
     return dict(logits=logits, idx=idx, w=w, margin=margin, counts=counts, out=out)
+
+
+def combine(cfg, y_rows, slot_row, w):
+    """out [T,H] (float64) from expert rows in the row space (see permute)."""
+    slot_row = np.ascontiguousarray(slot_row, dtype=np.int32)
+    T = slot_row.shape[0]
+    y_rows = np.ascontiguousarray(y_rows, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    if y_rows.shape[0] < T * cfg.k + cfg.S * T or y_rows.shape[1] != cfg.H:
+        raise ValueError("y_rows must be [T*k + S*T, H]")
+    out = np.empty((T, cfg.H), dtype=np.float64)
+    L = _layer(cfg)
+    _load().oracle_combine(ctypes.byref(L), T, _ptr(y_rows), _ptr(slot_row), _ptr(w), _ptr(out))
+    return out
 
 
 def moe_layer_params(H, E, S, I):

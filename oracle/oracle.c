@@ -415,6 +415,29 @@ int oracle_forward_tokens(const oracle_layer* L, int64_t n_tok, const int64_t* t
   return bad ? -1 : 0;
 }
 
+/* Combine over the row space: out[t,:] = sum_j w[t,j] * y_rows[slot_row[t,j],:]
+ * (empty slots skipped) + sum_s y_rows[T*k + s*T + t,:], in double. */
+int oracle_combine(const oracle_layer* L, int64_t T, const double* y_rows, const int32_t* slot_row, const double* w,
+                   double* out) {
+  const int64_t H = L->H;
+  const int k = L->k, S = L->S;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* o = out + t * H;
+    for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = slot_row[t * k + j];
+      if (r < 0) continue;
+      for (int64_t n = 0; n < H; ++n) o[n] += w[t * k + j] * y_rows[(int64_t)r * H + n];
+    }
+    for (int s = 0; s < S; ++s) {
+      const int64_t r = T * k + (int64_t)s * T + t;
+      for (int64_t n = 0; n < H; ++n) o[n] += y_rows[r * H + n];
+    }
+  }
+  return 0;
+}
+
 /* ---- parameter arithmetic ---------------------------------------------------- */
 /* One MoE layer: router E*H plus (E+S) experts of three H x I matrices. */
 int64_t oracle_moe_layer_params(int64_t H, int64_t E, int64_t S, int64_t I) { return E * H + (E + S) * 3 * H * I; }

@@ -1,0 +1,206 @@
+"""Python binding of libmoe.so, the gfx950 sparse MoE FFN layer (include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe.so.  torch supplies device memory and the stream: outputs not passed in
+are allocated with torch.empty, and every call enqueues on
+torch.cuda.current_stream() unless a stream is given.  There is no fallback:
+if libmoe.so is missing or cannot be loaded, using the binding raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
+          -4: "MOE_ERR_HIP"}
+
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "moe_last_error", "moe_version", "moe_timing_enable", "moe_timing_read", "moe_kernel_name")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (STATUS.get(status, status), msg))
+        self.status = status
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [("hidden_size", ctypes.c_int32), ("n_routed_experts", ctypes.c_int32),
+                ("n_shared_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("moe_intermediate_size", ctypes.c_int32),
+                ("scoring", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_float), ("capacity_factor", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+def make_config(shape, out_dtype=None):
+    """moe_config from a layer description (attributes H, E, S, k, G,
+    topk_group, I, scoring, renorm, scale, capacity_factor, dtype)."""
+    dt = MOE_F32 if shape.dtype == "f32" else MOE_BF16
+    od = dt if out_dtype is None else (MOE_F32 if out_dtype in ("f32", torch.float32, MOE_F32) else MOE_BF16)
+    return moe_config(shape.H, shape.E, shape.S, shape.k, shape.G, shape.topk_group, shape.I,
+                      MOE_SCORE_SIGMOID if shape.scoring == "sigmoid" else MOE_SCORE_SOFTMAX,
+                      1 if shape.renorm else 0, float(shape.scale), float(shape.capacity_factor), dt, od)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so (torch is imported first so that the library binds
+    to the HIP runtime torch already loaded)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmoe.so is not built (run __graft_entry__.build() or "
+                              "python -m routing_expert_ffn_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        C = ctypes.POINTER(moe_config)
+        for name in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
+                     "moe_forward", "moe_timing_enable", "moe_timing_read"):
+            getattr(L, name).restype = ctypes.c_int
+        L.moe_workspace_size.argtypes = [C, I64, ctypes.POINTER(SZ)]
+        L.moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_permute.argtypes = [C, I64, P, P, P, P, P, P, SZ, P]
+        L.moe_expert_ffn.argtypes = [C, I64, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_combine.argtypes = [C, I64, P, P, P, P, P]
+        L.moe_forward.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_version.restype = ctypes.c_char_p
+        L.moe_version.argtypes = []
+        L.moe_timing_enable.argtypes = [I32]
+        L.moe_timing_read.argtypes = [P, P, I32]
+        L.moe_kernel_name.restype = ctypes.c_char_p
+        L.moe_kernel_name.argtypes = [I32]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def version():
+    return lib().moe_version().decode()
+
+
+def workspace_size(cfg, T):
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), int(T), ctypes.byref(n)))
+    return n.value
+
+
+def workspace(cfg, T, device="cuda"):
+    return torch.empty(max(workspace_size(cfg, T), 256), dtype=torch.uint8, device=device)
+
+
+def _dev(t):
+    return t.device if t is not None else torch.device("cuda")
+
+
+def route(cfg, T, x=None, w_router=None, logit_bias=None, sel_bias=None, logits_in=None, logits_out=None,
+          topk_idx=None, topk_w=None, expert_counts=None, ws=None, stream=None):
+    """-> (topk_idx [T,k] int32, topk_w [T,k] fp32)"""
+    dev = _dev(x if x is not None else logits_in)
+    k = cfg.top_k
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if ws is None and cfg.capacity_factor > 0:
+        ws = workspace(cfg, T, dev)
+    _check(lib().moe_route(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(sel_bias), _p(logits_in),
+                           _p(logits_out), _p(topk_idx), _p(topk_w), _p(expert_counts), _p(ws),
+                           0 if ws is None else ws.numel(), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def permute(cfg, topk_idx, ws=None, stream=None):
+    """-> (expert_counts [E], expert_offsets [E+1], row_token [T*k+S*T], slot_row [T,k])"""
+    T = topk_idx.shape[0]
+    dev = topk_idx.device
+    E, k, S = cfg.n_routed_experts, cfg.top_k, cfg.n_shared_experts
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(T * k + S * T, dtype=torch.int32, device=dev)
+    slot_row = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(cfg, T, dev)
+    _check(lib().moe_permute(ctypes.byref(cfg), T, _p(topk_idx), _p(counts), _p(offsets), _p(row_token),
+                             _p(slot_row), _p(ws), ws.numel(), _stream(stream)))
+    return counts, offsets, row_token, slot_row
+
+
+def expert_ffn(cfg, x, w_gate, w_up, w_down, expert_offsets, row_token, y_rows=None, ws=None, stream=None):
+    """-> y_rows [T*k+S*T, H] (input dtype)"""
+    T = x.shape[0]
+    rows = T * cfg.top_k + cfg.n_shared_experts * T
+    if y_rows is None:
+        y_rows = torch.empty((rows, cfg.hidden_size), dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = workspace(cfg, T, x.device)
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(w_up), _p(w_down), _p(expert_offsets),
+                                _p(row_token), _p(y_rows), _p(ws), ws.numel(), _stream(stream)))
+    return y_rows
+
+
+def combine(cfg, T, y_rows, slot_row, topk_w, out=None, stream=None):
+    """-> out [T,H] in cfg.out_dtype"""
+    if out is None:
+        dt = torch.float32 if cfg.out_dtype == MOE_F32 else torch.bfloat16
+        out = torch.empty((T, cfg.hidden_size), dtype=dt, device=y_rows.device)
+    _check(lib().moe_combine(ctypes.byref(cfg), T, _p(y_rows), _p(slot_row), _p(topk_w), _p(out),
+                             _stream(stream)))
+    return out
+
+
+def forward(cfg, x, w_router, w_gate, w_up, w_down, logit_bias=None, sel_bias=None, out=None, topk_idx=None,
+            topk_w=None, expert_counts=None, logits_out=None, ws=None, stream=None):
+    """The whole layer; -> out [T,H] in cfg.out_dtype."""
+    T = x.shape[0]
+    if out is None:
+        dt = torch.float32 if cfg.out_dtype == MOE_F32 else torch.bfloat16
+        out = torch.empty((T, cfg.hidden_size), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(cfg, T, x.device)
+    _check(lib().moe_forward(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(sel_bias), _p(w_gate),
+                             _p(w_up), _p(w_down), _p(out), _p(topk_idx), _p(topk_w), _p(expert_counts),
+                             _p(logits_out), _p(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def timing_enable(max_launches):
+    _check(lib().moe_timing_enable(int(max_launches)))
+
+
+def timing_read(n_kernels=16):
+    """-> {kernel name: (total ms, launches)} for the launches recorded since
+    timing_enable (waits for them)."""
+    ms = (ctypes.c_double * n_kernels)()
+    cnt = (ctypes.c_int64 * n_kernels)()
+    _check(lib().moe_timing_read(ms, cnt, n_kernels))
+    out = {}
+    for i in range(n_kernels):
+        name = lib().moe_kernel_name(i)
+        if name is None:
+            break
+        if cnt[i]:
+            out[name.decode()] = (ms[i], cnt[i])
+    return out

@@ -1,0 +1,498 @@
+// C ABI of the MoE layer (include/moe.h): validation, workspace layout and
+// launch sequencing on the caller's stream.  No device memory is allocated
+// here and nothing synchronises the host except moe_timing_read.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return MOE_ERR_HIP;
+}
+
+// ---- per-kernel timing -------------------------------------------------------
+struct Timing {
+  int max = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> ids;
+};
+Timing g_timing;
+
+template <class F>
+hipError_t timed(int id, hipStream_t s, F&& f) {
+  if (g_timing.max > 0 && g_timing.used < g_timing.max) {
+    const int slot = g_timing.used++;
+    hipEventRecord(g_timing.ev[2 * slot], s);
+    const hipError_t err = f();
+    hipEventRecord(g_timing.ev[2 * slot + 1], s);
+    g_timing.ids[slot] = id;
+    return err;
+  }
+  return f();
+}
+
+// ---- configuration -------------------------------------------------------------
+struct Dims {
+  int64_t T;
+  int H, E, S, k, G, gsz, topk_group, I, scoring, renorm, dtype, out_dtype;
+  float scale;
+  int capacity;   // <= 0: unlimited
+  int n_allowed;
+  int esz;        // bytes per input element
+};
+
+moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+  d.T = T;
+  d.H = c->hidden_size;
+  d.E = c->n_routed_experts;
+  d.S = c->n_shared_experts;
+  d.k = c->top_k;
+  d.G = c->n_group;
+  d.topk_group = c->topk_group;
+  d.I = c->moe_intermediate_size;
+  d.scoring = c->scoring;
+  d.renorm = c->norm_topk_prob ? 1 : 0;
+  d.scale = c->routed_scaling_factor;
+  d.dtype = c->dtype;
+  d.out_dtype = c->out_dtype;
+  if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32 or MOE_BF16");
+  if (d.out_dtype != MOE_F32 && d.out_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_F32 or MOE_BF16");
+  if (d.scoring != MOE_SCORE_SOFTMAX && d.scoring != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "scoring must be MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID");
+  if (d.H <= 0 || d.I <= 0) return fail(MOE_ERR_INVALID_ARG, "hidden_size and moe_intermediate_size must be > 0");
+  if (d.E < 1) return fail(MOE_ERR_INVALID_ARG, "n_routed_experts must be >= 1");
+  if (d.E > 512) return fail(MOE_ERR_UNSUPPORTED, "n_routed_experts > 512 is not supported");
+  if (d.S < 0) return fail(MOE_ERR_INVALID_ARG, "n_shared_experts must be >= 0");
+  if (d.k < 1 || d.k > d.E) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, n_routed_experts]");
+  if (d.k > 32) return fail(MOE_ERR_UNSUPPORTED, "top_k > 32 is not supported");
+  if (d.G < 1 || d.E % d.G != 0) return fail(MOE_ERR_INVALID_ARG, "n_group must divide n_routed_experts");
+  if (d.G > 32) return fail(MOE_ERR_UNSUPPORTED, "n_group > 32 is not supported");
+  d.gsz = d.E / d.G;
+  if (d.G > 1 && d.gsz < 2) return fail(MOE_ERR_INVALID_ARG, "groups need at least 2 experts");
+  if (d.topk_group < 1 || d.topk_group > d.G) return fail(MOE_ERR_INVALID_ARG, "topk_group must be in [1, n_group]");
+  d.n_allowed = d.G > 1 ? d.topk_group * d.gsz : d.E;
+  if (d.k > d.n_allowed) return fail(MOE_ERR_INVALID_ARG, "top_k exceeds the experts of the kept groups");
+  if (!std::isfinite(d.scale)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling_factor must be finite");
+  if (!std::isfinite(c->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+  if (d.dtype == MOE_BF16) {
+    if (d.H % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need hidden_size % 256 == 0");
+    if (d.I % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need moe_intermediate_size % 128 == 0");
+  } else {
+    if (d.H % 32 != 0) return fail(MOE_ERR_UNSUPPORTED, "fp32 layers need hidden_size % 32 == 0");
+    if (d.I % 32 != 0) return fail(MOE_ERR_UNSUPPORTED, "fp32 layers need moe_intermediate_size % 32 == 0");
+  }
+  d.esz = d.dtype == MOE_BF16 ? 2 : 4;
+  const int64_t rows = T * d.k + (int64_t)d.S * T;
+  if (rows > 0x7FFFFFFF || T * (int64_t)d.E > 0x7FFFFFFF)
+    return fail(MOE_ERR_UNSUPPORTED, "T*(k+S) and T*E must fit in int32");
+  d.capacity = 0;
+  if (c->capacity_factor > 0.0f) {
+    // C = ceil(((cf*T)*k)/E) evaluated in IEEE double, left to right
+    const double cap = std::ceil((double)c->capacity_factor * (double)T * (double)d.k / (double)d.E);
+    if (cap > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "capacity too large");
+    d.capacity = (int)cap;
+    if (d.capacity < 1 && T > 0) d.capacity = 1;
+  }
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t logits, cand, idx, w, counts, offsets, slot_row, row_token, chunk_cnt, chunk_base, seg_start, seg_len,
+      mt_prefix, h, y, total;
+};
+
+Layout layout_of(const Dims& d) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t T = (size_t)d.T, E = d.E, S = d.S, k = d.k;
+  const size_t rows = T * k + S * T;
+  const size_t nchunks = (T + 63) / 64;
+  L.logits = take(T * E * 4);
+  L.cand = take(d.capacity > 0 ? T * (size_t)d.n_allowed * 4 : 0);
+  L.idx = take(T * k * 4);
+  L.w = take(T * k * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.slot_row = take(T * k * 4);
+  L.row_token = take(rows * 4);
+  L.chunk_cnt = take(nchunks * E * 4);
+  L.chunk_base = take(nchunks * E * 4);
+  L.seg_start = take((E + S) * 4);
+  L.seg_len = take((E + S) * 4);
+  L.mt_prefix = take((E + S + 1) * 4);
+  L.h = take(rows * (size_t)d.I * d.esz);
+  L.y = take(rows * (size_t)d.H * d.esz);
+  L.total = off;
+  return L;
+}
+
+template <class P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_ws(const Dims& d, void* ws, size_t ws_bytes, Layout& L) {
+  L = layout_of(d);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes, got " +
+                                       std::to_string(ws_bytes));
+  return MOE_OK;
+}
+
+RouteParams route_params(const Dims& d) {
+  RouteParams p;
+  p.T = (int)d.T;
+  p.H = d.H;
+  p.E = d.E;
+  p.k = d.k;
+  p.G = d.G;
+  p.gsz = d.gsz;
+  p.topk_group = d.topk_group;
+  p.scoring = d.scoring;
+  p.renorm = d.renorm;
+  p.scale = d.scale;
+  p.capacity = d.capacity;
+  p.n_allowed = d.n_allowed;
+  return p;
+}
+
+// ---- stages (arguments already validated) -----------------------------------
+moe_status do_route(const Dims& d, const void* x, const void* w_router, const float* logit_bias,
+                    const float* sel_bias, const float* logits_in, float* logits_out, int32_t* topk_idx,
+                    float* topk_w, int32_t* counts, void* ws, const Layout& L, hipStream_t s) {
+  RouterArgs a{};
+  a.p = route_params(d);
+  a.x = x;
+  a.w_router = w_router;
+  a.logit_bias = logit_bias;
+  a.sel_bias = sel_bias;
+  a.logits_in = logits_in;
+  a.logits_out = logits_out;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.counts = nullptr;
+  hipError_t e;
+  if (d.capacity > 0) {
+    float* lg = logits_out ? logits_out : at<float>(ws, L.logits);
+    if (logits_in) lg = const_cast<float*>(logits_in);
+    a.logits_out = logits_in ? nullptr : lg;
+    a.cand = at<int32_t>(ws, L.cand);
+    e = timed(K_ROUTER, s, [&] { return launch_router(a, d.dtype, s); });
+    if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+    if (logits_in && logits_out) {
+      e = hipMemcpyAsync(logits_out, logits_in, sizeof(float) * d.T * d.E, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "logits copy");
+    }
+    CapacityArgs c{};
+    c.p = a.p;
+    c.logits = lg;
+    c.cand = a.cand;
+    c.topk_idx = topk_idx;
+    c.topk_w = topk_w;
+    c.counts = counts;
+    e = timed(K_CAPACITY, s, [&] { return launch_capacity(c, s); });
+    if (e != hipSuccess) return hip_fail(e, "capacity kernel launch");
+    return MOE_OK;
+  }
+  if (counts) {
+    e = timed(K_FILL, s, [&] { return launch_fill_i32(counts, d.E, 0, s); });
+    if (e != hipSuccess) return hip_fail(e, "fill kernel launch");
+    a.counts = counts;
+  }
+  if (logits_in && logits_out) {
+    e = hipMemcpyAsync(logits_out, logits_in, sizeof(float) * d.T * d.E, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "logits copy");
+    a.logits_out = nullptr;
+  }
+  e = timed(K_ROUTER, s, [&] { return launch_router(a, d.dtype, s); });
+  if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+  return MOE_OK;
+}
+
+moe_status do_permute(const Dims& d, const int32_t* topk_idx, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                      int32_t* slot_row, void* ws, const Layout& L, hipStream_t s) {
+  PermuteArgs a{};
+  a.T = (int)d.T;
+  a.E = d.E;
+  a.k = d.k;
+  a.S = d.S;
+  a.nchunks = (int)((d.T + 63) / 64);
+  a.topk_idx = topk_idx;
+  a.chunk_cnt = at<int32_t>(ws, L.chunk_cnt);
+  a.chunk_base = at<int32_t>(ws, L.chunk_base);
+  a.counts = counts;
+  a.offsets = offsets;
+  a.row_token = row_token;
+  a.slot_row = slot_row;
+  hipError_t e = timed(K_PERM_COUNT, s, [&] { return launch_perm_count(a, s); });
+  if (e != hipSuccess) return hip_fail(e, "permute count launch");
+  e = timed(K_PERM_SCAN, s, [&] { return launch_perm_scan(a, s); });
+  if (e != hipSuccess) return hip_fail(e, "permute scan launch");
+  e = timed(K_PERM_SCATTER, s, [&] { return launch_perm_scatter(a, s); });
+  if (e != hipSuccess) return hip_fail(e, "permute scatter launch");
+  return MOE_OK;
+}
+
+moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                  const int32_t* offsets, const int32_t* row_token, void* y_rows, void* ws, const Layout& L,
+                  hipStream_t s) {
+  const int BM = gemm_bm(d.dtype);
+  ScheduleArgs sa{};
+  sa.T = (int)d.T;
+  sa.E = d.E;
+  sa.S = d.S;
+  sa.k = d.k;
+  sa.BM = BM;
+  sa.offsets = offsets;
+  sa.seg_start = at<int32_t>(ws, L.seg_start);
+  sa.seg_len = at<int32_t>(ws, L.seg_len);
+  sa.mt_prefix = at<int32_t>(ws, L.mt_prefix);
+  hipError_t e = timed(K_SCHEDULE, s, [&] { return launch_schedule(sa, s); });
+  if (e != hipSuccess) return hip_fail(e, "schedule launch");
+  const int64_t bound = gemm_mtile_bound((int)d.T, d.E, d.S, d.k, BM);
+  GemmArgs g{};
+  g.n_exp = d.E + d.S;
+  g.seg_start = sa.seg_start;
+  g.seg_len = sa.seg_len;
+  g.mt_prefix = sa.mt_prefix;
+  g.row_token = row_token;
+  void* h = at<void>(ws, L.h);
+  // gate/up + SwiGLU
+  g.K = d.H;
+  g.N = d.I;
+  g.n_tiles = d.dtype == MOE_BF16 ? d.I / 128 : d.I / 32;
+  g.a = x;
+  g.b0 = w_gate;
+  g.b1 = w_up;
+  g.c = h;
+  if (bound * g.n_tiles > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "too many GEMM tiles");
+  e = timed(K_GATEUP, s, [&] { return launch_gateup(g, d.dtype, bound, s); });
+  if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
+  // down
+  g.K = d.I;
+  g.N = d.H;
+  g.n_tiles = d.dtype == MOE_BF16 ? d.H / 256 : d.H / 32;
+  g.a = h;
+  g.b0 = w_down;
+  g.b1 = nullptr;
+  g.c = y_rows;
+  if (bound * g.n_tiles > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "too many GEMM tiles");
+  e = timed(K_DOWN, s, [&] { return launch_down(g, d.dtype, bound, s); });
+  if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
+  return MOE_OK;
+}
+
+moe_status do_combine(const Dims& d, const void* y_rows, const int32_t* slot_row, const float* topk_w, void* out,
+                      hipStream_t s) {
+  CombineArgs a{};
+  a.T = (int)d.T;
+  a.H = d.H;
+  a.k = d.k;
+  a.S = d.S;
+  a.y_rows = y_rows;
+  a.slot_row = slot_row;
+  a.topk_w = topk_w;
+  a.out = out;
+  const hipError_t e = timed(K_COMBINE, s, [&] { return launch_combine(a, d.dtype, d.out_dtype, s); });
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+// ---- kernel names --------------------------------------------------------------
+const char* kernel_name(int id) {
+  static const char* names[K_COUNT] = {"fill",          "router",   "capacity", "permute_count",
+                                       "permute_scan",  "permute_scatter", "schedule", "gateup_swiglu",
+                                       "down",          "combine"};
+  return (id >= 0 && id < K_COUNT) ? names[id] : nullptr;
+}
+
+// ---- exported ------------------------------------------------------------------
+extern "C" {
+
+moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes) {
+  Dims d;
+  const moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout_of(d).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* logit_bias,
+                     const float* sel_bias, const float* logits_in, float* logits_out, int32_t* topk_idx,
+                     float* topk_w, int32_t* expert_counts, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits_in && (!x || !w_router)) return fail(MOE_ERR_INVALID_ARG, "x and w_router are required without logits_in");
+  if (!logits_in && (!aligned16(x) || !aligned16(w_router)))
+    return fail(MOE_ERR_INVALID_ARG, "x and w_router must be 16-byte aligned");
+  if (!topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "topk_idx and topk_w are required");
+  Layout L{};
+  if (d.capacity > 0) {
+    st = check_ws(d, ws, ws_bytes, L);
+    if (st != MOE_OK) return st;
+  }
+  return do_route(d, x, w_router, logit_bias, sel_bias, logits_in, logits_out, topk_idx, topk_w, expert_counts, ws, L,
+                  static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row, void* ws, size_t ws_bytes,
+                       void* stream) {
+  Dims d;
+  moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  if (!expert_counts || !expert_offsets) return fail(MOE_ERR_INVALID_ARG, "expert_counts and expert_offsets are required");
+  if (T > 0 && (!topk_idx || !row_token || !slot_row))
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx, row_token and slot_row are required");
+  Layout L{};
+  st = check_ws(d, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    // empty batch: every expert has zero rows
+    hipError_t e = launch_fill_i32(expert_counts, d.E, 0, s);
+    if (e == hipSuccess) e = launch_fill_i32(expert_offsets, d.E + 1, 0, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "fill kernel launch");
+  }
+  return do_permute(d, topk_idx, expert_counts, expert_offsets, row_token, slot_row, ws, L, s);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const void* w_gate, const void* w_up,
+                          const void* w_down, const int32_t* expert_offsets, const int32_t* row_token, void* y_rows,
+                          void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate || !w_up || !w_down || !expert_offsets || !row_token || !y_rows)
+    return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(y_rows))
+    return fail(MOE_ERR_INVALID_ARG, "x, weights and y_rows must be 16-byte aligned");
+  Layout L{};
+  st = check_ws(d, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  return do_ffn(d, x, w_gate, w_up, w_down, expert_offsets, row_token, y_rows, ws, L, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, const int32_t* slot_row,
+                       const float* topk_w, void* out, void* stream) {
+  Dims d;
+  moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!y_rows || !slot_row || !topk_w || !out) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+  if (!aligned16(y_rows) || !aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "y_rows and out must be 16-byte aligned");
+  return do_combine(d, y_rows, slot_row, topk_w, out, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* logit_bias,
+                       const float* sel_bias, const void* w_gate, const void* w_up, const void* w_down, void* out,
+                       int32_t* topk_idx, float* topk_w, int32_t* expert_counts, float* logits_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(out))
+    return fail(MOE_ERR_INVALID_ARG, "x, weights and out must be 16-byte aligned");
+  Layout L{};
+  st = check_ws(d, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* w = topk_w ? topk_w : at<float>(ws, L.w);
+  int32_t* counts = expert_counts ? expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  int32_t* slot_row = at<int32_t>(ws, L.slot_row);
+  void* y = at<void>(ws, L.y);
+  st = do_route(d, x, w_router, logit_bias, sel_bias, nullptr, logits_out, idx, w, nullptr, ws, L, s);
+  if (st != MOE_OK) return st;
+  st = do_permute(d, idx, counts, offsets, row_token, slot_row, ws, L, s);
+  if (st != MOE_OK) return st;
+  st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y, ws, L, s);
+  if (st != MOE_OK) return st;
+  return do_combine(d, y, slot_row, w, out, s);
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "routing_expert_ffn_amd 0.1.0 (gfx950)"; }
+
+moe_status moe_timing_enable(int32_t max_launches) {
+  for (hipEvent_t e : g_timing.ev) hipEventDestroy(e);
+  g_timing.ev.clear();
+  g_timing.ids.clear();
+  g_timing.max = 0;
+  g_timing.used = 0;
+  if (max_launches <= 0) return MOE_OK;
+  g_timing.ev.resize(2 * (size_t)max_launches);
+  g_timing.ids.resize(max_launches);
+  for (auto& e : g_timing.ev) {
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+  }
+  g_timing.max = max_launches;
+  return MOE_OK;
+}
+
+moe_status moe_timing_read(double* ms, int64_t* launches, int32_t n_kernels) {
+  if (!ms || !launches || n_kernels < 0) return fail(MOE_ERR_INVALID_ARG, "bad timing buffers");
+  for (int i = 0; i < n_kernels; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  for (int slot = 0; slot < g_timing.used; ++slot) {
+    hipError_t err = hipEventSynchronize(g_timing.ev[2 * slot + 1]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
+    float t = 0.0f;
+    err = hipEventElapsedTime(&t, g_timing.ev[2 * slot], g_timing.ev[2 * slot + 1]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventElapsedTime");
+    const int id = g_timing.ids[slot];
+    if (id < n_kernels) {
+      ms[id] += t;
+      launches[id] += 1;
+    }
+  }
+  g_timing.used = 0;
+  return MOE_OK;
+}
+
+const char* moe_kernel_name(int32_t id) { return kernel_name(id); }
+
+}  // extern "C"

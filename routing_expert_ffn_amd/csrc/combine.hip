@@ -1,0 +1,102 @@
+// Gate-weighted combine of the MoE layer for gfx950:
+//   out[t] = sum_j w[t,j] * y_rows[slot_row[t,j]] + sum_s y_rows[T*k + s*T + t]
+// ("15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the
+// router sketch's last line: weighted routed experts plus the shared expert).
+// One workgroup per token; 16-byte loads of y rows, fp32 accumulation in a
+// fixed order (slots, then shared experts), so the result is deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float (&v)[8]) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+  }
+  static __device__ __forceinline__ void store(bf16* p, const float (&v)[8]) {
+    bf16x8 x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8*>(p) = x;
+  }
+};
+template <>
+struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[i + 4] = b[i];
+    }
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[8]) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = v[i];
+      b[i] = v[i + 4];
+    }
+    *reinterpret_cast<f32x4*>(p) = a;
+    *reinterpret_cast<f32x4*>(p + 4) = b;
+  }
+};
+
+template <typename TY, typename TO>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  __shared__ int32_t srow[MOE_MAX_TOPK];
+  __shared__ float sw[MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  if (threadIdx.x < a.k) {
+    srow[threadIdx.x] = a.slot_row[(int64_t)t * a.k + threadIdx.x];
+    sw[threadIdx.x] = a.topk_w[(int64_t)t * a.k + threadIdx.x];
+  }
+  __syncthreads();
+  const TY* y = static_cast<const TY*>(a.y_rows);
+  TO* out = static_cast<TO*>(a.out) + (int64_t)t * a.H;
+  const int64_t shared0 = (int64_t)a.T * a.k + t;
+  for (int c = threadIdx.x * 8; c < a.H; c += blockDim.x * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < a.k; ++j) {
+      const int r = srow[j];
+      if (r < 0) continue;
+      const float w = sw[j];
+      float v[8];
+      Vec8<TY>::load(y + (int64_t)r * a.H + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += w * v[i];
+    }
+    for (int s = 0; s < a.S; ++s) {
+      float v[8];
+      Vec8<TY>::load(y + (shared0 + (int64_t)s * a.T) * a.H + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    Vec8<TO>::store(out + c, acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  dim3 grid(a.T), block(256);
+  if (dtype == 1) {
+    if (out_dtype == 1)
+      hipLaunchKernelGGL((combine_kernel<bf16, bf16>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<bf16, float>), grid, block, 0, s, a);
+  } else {
+    if (out_dtype == 1)
+      hipLaunchKernelGGL((combine_kernel<float, bf16>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}

@@ -1,0 +1,83 @@
+// Internal types and helpers of the gfx950 MoE kernels (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define MOE_WAVE 64
+
+// Largest routed expert count the router kernels hold in registers (8 per lane).
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_GROUPS 32
+#define MOE_MAX_TOPK 32
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) {
+  return v;
+}
+template <>
+__device__ __forceinline__ float to_f32<bf16>(bf16 v) {
+  return (float)v;
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) {
+  return v;
+}
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float v) {
+  return (bf16)v;  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Maximum of a 64-bit key over the wavefront (butterfly; every lane gets it).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 1; off < MOE_WAVE; off <<= 1) {
+    uint64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 1; off < MOE_WAVE; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 1; off < MOE_WAVE; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Order-preserving map of an fp32 value to uint32 (larger float -> larger int).
+// -0 is first turned into +0 so that the two zeros tie.
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  f = f + 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Rank key: higher score first, lower expert index on equal scores.  Key 0 is
+// "nothing" (never produced for a real expert: ordered_bits of a finite
+// float is never 0 in the high word together with index slot 0xFFFFFFFF).
+__device__ __forceinline__ uint64_t rank_key(float score, int e) {
+  return ((uint64_t)ordered_bits(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu)); }

@@ -1,0 +1,111 @@
+// Launchers of the gfx950 MoE kernels (internal; used by api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Routing description handed to the selection code.
+struct RouteParams {
+  int T, H, E, k;
+  int G, gsz, topk_group;
+  int scoring;   // 0 softmax, 1 sigmoid
+  int renorm;
+  float scale;
+  int capacity;  // <= 0: unlimited
+  int n_allowed; // experts a token may pick from after the group limit
+};
+
+struct RouterArgs {
+  RouteParams p;
+  const void* x;            // [T,H] (ignored when logits_in)
+  const void* w_router;     // [E,H]
+  const float* logit_bias;  // [E] or null
+  const float* sel_bias;    // [E] or null
+  const float* logits_in;   // [T,E] or null: route these logits
+  float* logits_out;        // [T,E] or null
+  int32_t* topk_idx;        // [T,k] (unused in capacity mode)
+  float* topk_w;            // [T,k]
+  int32_t* counts;          // [E] atomically incremented, or null
+  int32_t* cand;            // capacity mode: [T,n_allowed] experts in rank order
+};
+
+struct CapacityArgs {
+  RouteParams p;
+  const float* logits;      // [T,E]
+  const int32_t* cand;      // [T,n_allowed]
+  int32_t* topk_idx;        // [T,k]
+  float* topk_w;            // [T,k]
+  int32_t* counts;          // [E] or null
+};
+
+struct PermuteArgs {
+  int T, E, k, S, nchunks;
+  const int32_t* topk_idx;  // [T,k]
+  int32_t* chunk_cnt;       // [nchunks,E]
+  int32_t* chunk_base;      // [nchunks,E]
+  int32_t* counts;          // [E]
+  int32_t* offsets;         // [E+1]
+  int32_t* row_token;       // [T*k + S*T]
+  int32_t* slot_row;        // [T,k]
+};
+
+// Row segments of the experts (routed then shared) and their m-tile prefix.
+struct ScheduleArgs {
+  int T, E, S, k, BM;
+  const int32_t* offsets;   // [E+1]
+  int32_t* seg_start;       // [E+S]
+  int32_t* seg_len;         // [E+S]
+  int32_t* mt_prefix;       // [E+S+1]
+};
+
+struct GemmArgs {
+  int K, N;                 // reduction length, output columns of this GEMM
+  int n_exp;                // E + S
+  int n_tiles;              // column tiles per m-tile
+  const void* a;            // gate/up: x [T,H]; down: h [rows,I]
+  const int32_t* row_token; // gate/up: token of every row
+  const void* b0;           // gate/up: w_gate; down: w_down
+  const void* b1;           // gate/up: w_up; down: unused
+  void* c;                  // gate/up: h [rows,I]; down: y_rows [rows,H]
+  const int32_t* seg_start;
+  const int32_t* seg_len;
+  const int32_t* mt_prefix;
+};
+
+struct CombineArgs {
+  int T, H, k, S;
+  const void* y_rows;       // [T*k+S*T, H]
+  const int32_t* slot_row;  // [T,k]
+  const float* topk_w;      // [T,k]
+  void* out;                // [T,H]
+};
+
+// Kernel ids (for timing); names in kernel_names().
+enum KernelId {
+  K_FILL = 0,
+  K_ROUTER,
+  K_CAPACITY,
+  K_PERM_COUNT,
+  K_PERM_SCAN,
+  K_PERM_SCATTER,
+  K_SCHEDULE,
+  K_GATEUP,
+  K_DOWN,
+  K_COMBINE,
+  K_COUNT
+};
+
+const char* kernel_name(int id);
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s);
+hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s);
+hipError_t launch_perm_count(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_perm_scan(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_perm_scatter(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
+// Upper bound of the m-tiles of all experts (grid sizing without a host sync).
+int64_t gemm_mtile_bound(int T, int E, int S, int k, int BM);
+int gemm_bm(int dtype);
+hipError_t launch_gateup(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStream_t s);
+hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s);

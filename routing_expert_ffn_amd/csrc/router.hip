@@ -1,0 +1,420 @@
+// Fused router of the MoE layer for gfx950: router GEMM on the matrix cores,
+// scoring, group-limited top-k and gates, one wavefront per token in
+// registers; plus the serial capacity pass.
+//
+// What is computed ("15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家
+// 怎样选 8 个"; "MoE架构揭秘", section 3.1; "GPT-4 Has 1.8 Trillion Parameters.
+// It Uses 2% of Them Per Token", section 2.2):
+//   l = x W_r^T (+ logit_bias)
+//   softmax scoring: rank the fp32 logits; sigmoid scoring: rank
+//   c = fl32(sigmoid32(l) + sel_bias)
+//   G > 1: group score = fl32(best + second best c of the group), keep the
+//   topk_group best groups, rank only their experts
+//   top-k in rank order (ties: lower index), gates per moe.h
+//   capacity: tokens in order take their best-ranked allowed experts with room.
+//
+// This translation unit is compiled without floating-point contraction so the
+// fp32 sigmoid below is exactly the documented sequence of roundings.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+// e^z for z <= 0 from correctly rounded fp32 operations: n = rint(z*log2e),
+// r = z - n*ln2 (ln2 in two parts, fused), e^r by the degree-7 Taylor
+// polynomial in Horner form with fused multiply-adds, result scaled by 2^n.
+__device__ __forceinline__ float exp32_nonpos(float z) {
+  const float t = z * 0x1.715476p+0f;
+  const float n = __builtin_rintf(t);
+  float r = __builtin_fmaf(-n, 0x1.62e4p-1f, z);
+  r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
+  float q = 0x1.a01a02p-13f;
+  q = __builtin_fmaf(q, r, 0x1.6c16c2p-10f);
+  q = __builtin_fmaf(q, r, 0x1.111112p-7f);
+  q = __builtin_fmaf(q, r, 0x1.555556p-5f);
+  q = __builtin_fmaf(q, r, 0x1.555556p-3f);
+  q = __builtin_fmaf(q, r, 0x1p-1f);
+  q = __builtin_fmaf(q, r, 0x1p+0f);
+  q = __builtin_fmaf(q, r, 0x1p+0f);
+  return __builtin_amdgcn_ldexpf(q, (int)n);
+}
+
+// Selection sigmoid: logit clamped to [-80, 80] (keeps everything normal),
+// 1/(1+e^-l) for l >= 0 and e^l/(1+e^l) for l < 0.
+__device__ __forceinline__ float sigmoid32(float l) {
+  l = l > 80.0f ? 80.0f : l;
+  l = l < -80.0f ? -80.0f : l;
+  if (l >= 0.0f) {
+    const float e = exp32_nonpos(-l);
+    const float d = 1.0f + e;
+    return 1.0f / d;
+  }
+  const float e = exp32_nonpos(l);
+  const float d = 1.0f + e;
+  return e / d;
+}
+
+__device__ __forceinline__ float ordered_to_float(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Selection scores of one token: lane holds experts e = j*64 + lane.
+template <int NJ>
+__device__ __forceinline__ void token_scores(const RouteParams& p, const float* lrow, const float* sel_bias,
+                                             int lane, uint64_t (&key)[NJ]) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = j * MOE_WAVE + lane;
+    key[j] = 0;
+    if (e < p.E) {
+      const float l = lrow[e];
+      float c;
+      if (p.scoring == 1) {
+        const float s = sigmoid32(l);
+        const float b = sel_bias ? sel_bias[e] : 0.0f;
+        c = s + b;
+      } else {
+        c = l;
+      }
+      key[j] = rank_key(c, e);
+    }
+  }
+  if (p.G <= 1) return;
+  // group scores: best and second best key of each group (an equal value at
+  // another index counts as the second best)
+  const int gsz = p.gsz;
+  float my_gs = 0.0f;
+  for (int g = 0; g < p.G; ++g) {
+    uint64_t b1 = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * MOE_WAVE + lane;
+      if (key[j] && e / gsz == g && key[j] > b1) b1 = key[j];
+    }
+    b1 = wave_max_u64(b1);
+    uint64_t b2 = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * MOE_WAVE + lane;
+      if (key[j] && e / gsz == g && key[j] != b1 && key[j] > b2) b2 = key[j];
+    }
+    b2 = wave_max_u64(b2);
+    const float v1 = ordered_to_float((uint32_t)(b1 >> 32));
+    const float v2 = ordered_to_float((uint32_t)(b2 >> 32));
+    const float gs = v1 + v2;
+    if (lane == g) my_gs = gs;
+  }
+  uint64_t gkey = lane < p.G ? rank_key(my_gs, lane) : 0;
+  uint64_t kept = 0;
+  for (int i = 0; i < p.topk_group; ++i) {
+    const uint64_t m = wave_max_u64(gkey);
+    const int g = key_expert(m);
+    kept |= 1ull << g;
+    if (lane == g) gkey = 0;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = j * MOE_WAVE + lane;
+    if (key[j] && !((kept >> (e / gsz)) & 1ull)) key[j] = 0;
+  }
+}
+
+// Gate of the expert lane i holds for slot i (lanes >= k or empty slots: 0).
+template <int NJ>
+__device__ __forceinline__ float token_gate(const RouteParams& p, const float* lrow, int my_e, int lane) {
+  const bool mine = lane < p.k && my_e >= 0;
+  float g = 0.0f;
+  if (p.scoring == 1) {
+    const float s = mine ? sigmoid32(lrow[my_e]) : 0.0f;
+    if (p.renorm) {
+      const float tot = wave_sum_f32(s);
+      g = mine ? s / tot : 0.0f;
+    } else {
+      g = s;
+    }
+  } else if (p.renorm) {
+    // softmax renormalised over the selection = softmax of the chosen logits;
+    // the slot-0 expert has the largest chosen logit
+    const float l = mine ? lrow[my_e] : 0.0f;
+    const float m0 = __shfl(l, 0);
+    const float ex = mine ? expf(l - m0) : 0.0f;
+    const float tot = wave_sum_f32(ex);
+    g = mine ? ex / tot : 0.0f;
+  } else {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * MOE_WAVE + lane;
+      if (e < p.E) mx = fmaxf(mx, lrow[e]);
+    }
+    mx = wave_max_f32(mx);
+    float z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * MOE_WAVE + lane;
+      if (e < p.E) z += expf(lrow[e] - mx);
+    }
+    z = wave_sum_f32(z);
+    g = mine ? expf(lrow[my_e] - mx) / z : 0.0f;
+  }
+  return g * p.scale;
+}
+
+// Top-k of one token by repeated wavefront argmax; lane i ends with slot i.
+template <int NJ>
+__device__ __forceinline__ int token_topk(const RouteParams& p, uint64_t (&key)[NJ], int lane) {
+  int my_e = -1;
+  for (int i = 0; i < p.k; ++i) {
+    uint64_t local = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) local = key[j] > local ? key[j] : local;
+    const uint64_t m = wave_max_u64(local);
+    const int e = m ? key_expert(m) : -1;
+    if (lane == i) my_e = e;
+    if (e >= 0 && (e & (MOE_WAVE - 1)) == lane) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (j == (e >> 6)) key[j] = 0;
+    }
+  }
+  return my_e;
+}
+
+// Descending bitonic sort of the 64*NJ keys of the wavefront; element
+// i = j*64 + lane ends holding rank i.
+template <int NJ>
+__device__ __forceinline__ void wave_bitonic_desc(uint64_t (&key)[NJ], int lane) {
+  constexpr int N = NJ * MOE_WAVE;
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      uint64_t nk[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int i = j * MOE_WAVE + lane;
+        uint64_t other;
+        if (stride >= MOE_WAVE)
+          other = key[j ^ (stride / MOE_WAVE)];
+        else
+          other = __shfl_xor(key[j], stride);
+        const bool lower = (i & stride) == 0;
+        const bool desc = (i & size) == 0;
+        const bool keep_max = lower == desc;
+        const uint64_t mx = key[j] > other ? key[j] : other;
+        const uint64_t mn = key[j] > other ? other : key[j];
+        nk[j] = keep_max ? mx : mn;
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) key[j] = nk[j];
+    }
+  }
+}
+
+constexpr int kRouterTokens = 32;
+
+// One workgroup: 32 tokens x all experts.  The GEMM runs on 32x32 MFMA tiles
+// (wave w owns expert blocks w, w+4, ...), the tile of logits goes to LDS,
+// then each wave routes tokens w, w+4, ... .
+template <typename Tin, int NJ>
+__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
+  extern __shared__ float lds_logits[];
+  constexpr int EP = NJ * MOE_WAVE;
+  constexpr int NB = (2 * NJ + 3) / 4;  // 32-wide expert blocks per wave
+  const RouteParams& p = a.p;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  if (a.logits_in == nullptr) {
+    f32x16 acc[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+    const int tok = min(t0 + (lane & 31), p.T - 1);
+    const Tin* x = static_cast<const Tin*>(a.x);
+    const Tin* w = static_cast<const Tin*>(a.w_router);
+    if constexpr (sizeof(Tin) == 2) {
+      const Tin* xa = x + (int64_t)tok * p.H + (lane >> 5) * 8;
+      const Tin* wb[NB];
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const int e = min((wave + 4 * q) * 32 + (lane & 31), p.E - 1);
+        wb[q] = w + (int64_t)e * p.H + (lane >> 5) * 8;
+      }
+#pragma unroll 4
+      for (int k0 = 0; k0 < p.H; k0 += 16) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(xa + k0);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          if ((wave + 4 * q) * 32 < p.E) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(wb[q] + k0);
+            acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[q], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+      const float* xa = reinterpret_cast<const float*>(x) + (int64_t)tok * p.H + (lane >> 5);
+      const float* wb[NB];
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const int e = min((wave + 4 * q) * 32 + (lane & 31), p.E - 1);
+        wb[q] = reinterpret_cast<const float*>(w) + (int64_t)e * p.H + (lane >> 5);
+      }
+      for (int k0 = 0; k0 < p.H; k0 += 2) {
+        const float av = xa[k0];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          if ((wave + 4 * q) * 32 < p.E) acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, wb[q][k0], acc[q], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int col = (wave + 4 * q) * 32 + (lane & 31);
+      if ((wave + 4 * q) * 32 >= EP) continue;
+      const float lb = (a.logit_bias && col < p.E) ? a.logit_bias[col] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        lds_logits[row * EP + col] = acc[q][r] + lb;
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < kRouterTokens * EP; i += blockDim.x) {
+      const int r = i / EP, c = i % EP;
+      const int t = t0 + r;
+      lds_logits[i] = (t < p.T && c < p.E) ? a.logits_in[(int64_t)t * p.E + c] : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  if (a.logits_out) {
+    for (int i = threadIdx.x; i < kRouterTokens * p.E; i += blockDim.x) {
+      const int r = i / p.E, c = i % p.E;
+      const int t = t0 + r;
+      if (t < p.T) a.logits_out[(int64_t)t * p.E + c] = lds_logits[r * EP + c];
+    }
+  }
+
+  for (int r = wave; r < kRouterTokens; r += 4) {
+    const int t = t0 + r;
+    if (t >= p.T) break;
+    const float* lrow = lds_logits + r * EP;
+    uint64_t key[NJ];
+    token_scores<NJ>(p, lrow, a.sel_bias, lane, key);
+    if (p.capacity > 0) {
+      wave_bitonic_desc<NJ>(key, lane);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int i = j * MOE_WAVE + lane;
+        if (i < p.n_allowed) a.cand[(int64_t)t * p.n_allowed + i] = key_expert(key[j]);
+      }
+    } else {
+      const int my_e = token_topk<NJ>(p, key, lane);
+      const float g = token_gate<NJ>(p, lrow, my_e, lane);
+      if (lane < p.k) {
+        a.topk_idx[(int64_t)t * p.k + lane] = my_e;
+        a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
+        if (a.counts && my_e >= 0) atomicAdd(&a.counts[my_e], 1);
+      }
+    }
+  }
+}
+
+// Capacity pass: one wavefront serves the tokens in index order; lane r of a
+// step looks at rank base+r of the token's allowed experts, those with room
+// are taken in rank order until k are chosen.
+template <int NJ>
+__global__ __launch_bounds__(64) void capacity_kernel(CapacityArgs a) {
+  extern __shared__ int32_t lds_cnt[];  // [E] then 32 slots
+  int32_t* sel = lds_cnt + a.p.E;
+  const RouteParams& p = a.p;
+  const int lane = threadIdx.x;
+  for (int e = lane; e < p.E; e += MOE_WAVE) lds_cnt[e] = 0;
+  __syncthreads();
+  const int NA = p.n_allowed;
+  for (int t = 0; t < p.T; ++t) {
+    int got = 0;
+    for (int base = 0; base < NA && got < p.k; base += MOE_WAVE) {
+      const int r = base + lane;
+      const int e = r < NA ? a.cand[(int64_t)t * NA + r] : -1;
+      const bool room = e >= 0 && lds_cnt[e] < p.capacity;
+      const uint64_t m = __ballot(room);
+      const int need = p.k - got;
+      const int pre = __popcll(m & ((1ull << lane) - 1ull));
+      if (room && pre < need) {
+        lds_cnt[e] += 1;
+        sel[got + pre] = e;
+      }
+      const int avail = __popcll(m);
+      got += avail < need ? avail : need;
+      __syncthreads();
+    }
+    const int my_e = lane < got ? sel[lane] : -1;
+    const float* lrow = a.logits + (int64_t)t * p.E;
+    const float g = token_gate<NJ>(p, lrow, my_e, lane);
+    if (lane < p.k) {
+      a.topk_idx[(int64_t)t * p.k + lane] = my_e;
+      a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
+    }
+    __syncthreads();
+  }
+  if (a.counts)
+    for (int e = lane; e < p.E; e += MOE_WAVE) a.counts[e] = lds_cnt[e];
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+template <typename Tin, int NJ>
+hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
+  const int grid = (a.p.T + kRouterTokens - 1) / kRouterTokens;
+  const size_t lds = sizeof(float) * kRouterTokens * NJ * MOE_WAVE;
+  hipLaunchKernelGGL((router_kernel<Tin, NJ>), dim3(grid), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t launch_router_d(const RouterArgs& a, hipStream_t s) {
+  const int nj = (a.p.E + MOE_WAVE - 1) / MOE_WAVE;
+  if (nj <= 1) return launch_router_t<Tin, 1>(a, s);
+  if (nj <= 2) return launch_router_t<Tin, 2>(a, s);
+  if (nj <= 4) return launch_router_t<Tin, 4>(a, s);
+  return launch_router_t<Tin, 8>(a, s);
+}
+
+template <int NJ>
+hipError_t launch_capacity_t(const CapacityArgs& a, hipStream_t s) {
+  const size_t lds = sizeof(int32_t) * (a.p.E + MOE_MAX_TOPK);
+  hipLaunchKernelGGL((capacity_kernel<NJ>), dim3(1), dim3(64), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s) {
+  if (a.p.T <= 0) return hipSuccess;
+  return dtype == 1 ? launch_router_d<bf16>(a, s) : launch_router_d<float>(a, s);
+}
+
+hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s) {
+  if (a.p.T <= 0) return hipSuccess;
+  const int nj = (a.p.E + MOE_WAVE - 1) / MOE_WAVE;
+  if (nj <= 1) return launch_capacity_t<1>(a, s);
+  if (nj <= 2) return launch_capacity_t<2>(a, s);
+  if (nj <= 4) return launch_capacity_t<4>(a, s);
+  return launch_capacity_t<8>(a, s);
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}

@@ -1,0 +1,322 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
+
+Bars:
+ - routing indices, expert counts and the permutation: bit-exact given the
+   same fp32 logits;
+ - router logits: within 2e-4 absolute of the oracle's fp32-rounded exact dot
+   products (fp32 accumulation of bf16 products over H <= 7168);
+ - gates: within 1e-5 relative (fp32 gate arithmetic vs fp64);
+ - end to end: tokens whose oracle selection margin is below 1e-5 are left out
+   of the index comparison (their outputs are checked against the oracle run
+   with the GPU's selection); layer outputs within max-abs 2e-2 x RMS(output)
+   for bf16 layers and 1e-4 x RMS for fp32 layers, on the fp32-valued output;
+   a bf16-stored output additionally gets half a bf16 ulp of the reference.
+Capacity layers couple tokens through the expert counts, so their indices are
+compared in identical-logits mode (GPU logits fed to the oracle).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routing_expert_ffn_amd as moe
+from tests.hostdata import to_oracle
+from workloads import CONFIGS, TEST_SHAPES, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-5
+LOGIT_ATOL = 2e-4
+
+
+def gpu_available():
+    return torch.cuda.is_available()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def run_layer(shape, inp, out_dtype):
+    cfg = moe.make_config(shape, out_dtype=out_dtype)
+    T = inp["x"].shape[0]
+    dev = inp["x"].device
+    g = dict(
+        idx=torch.empty((T, shape.k), dtype=torch.int32, device=dev),
+        w=torch.empty((T, shape.k), dtype=torch.float32, device=dev),
+        counts=torch.empty((shape.E,), dtype=torch.int32, device=dev),
+        logits=torch.empty((T, shape.E), dtype=torch.float32, device=dev),
+    )
+    g["out"] = moe.forward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                           logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], topk_idx=g["idx"], topk_w=g["w"],
+                           expert_counts=g["counts"], logits_out=g["logits"])
+    torch.cuda.synchronize()
+    return {k: v.cpu() for k, v in g.items()}
+
+
+def bf16_half_ulp(v):
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 1e-30)))
+    return 0.5 * 2.0 ** (e - 7)
+
+
+def check_layer(shape, inp, g, tokens, out_dtype):
+    """Compare one GPU layer call with the oracle on `tokens`."""
+    x_h = to_oracle(inp["x"])
+    wr_h = to_oracle(inp["w_router"])
+    sb = to_oracle(inp["sel_bias"])
+    lb = to_oracle(inp["logit_bias"])
+    L = g["logits"].numpy()
+    idx = g["idx"].numpy()
+    # routing from identical logits: bit-exact for every token
+    oidx, ow, _, ocounts = oracle.select(shape, L, sb)
+    assert np.array_equal(idx, oidx), "routing differs from the oracle on identical logits"
+    assert np.array_equal(g["counts"].numpy(), ocounts)
+    np.testing.assert_allclose(g["w"].numpy(), ow, rtol=1e-5, atol=1e-6)
+    # logits against the oracle's own dot products
+    ol = oracle.router_logits(shape, x_h[tokens], wr_h, lb)
+    assert np.max(np.abs(L[tokens] - ol)) <= LOGIT_ATOL
+    if shape.capacity_factor > 0:
+        ref_idx, ref_w = oidx[tokens], ow[tokens]
+        keep = np.ones(len(tokens), bool)
+    else:
+        ref_idx, ref_w, ref_margin, _ = oracle.select(shape, ol, sb)
+        keep = ref_margin >= MARGIN
+        assert np.array_equal(idx[tokens][keep], ref_idx[keep]), "indices differ from the oracle"
+        ref_idx = np.where(keep[:, None], ref_idx, oidx[tokens])
+        ref_w = np.where(keep[:, None], ref_w, ow[tokens])
+
+    def get_expert(e):
+        return to_oracle(inp["w_gate"][e]), to_oracle(inp["w_up"][e]), to_oracle(inp["w_down"][e])
+
+    ref = oracle.forward_tokens(shape, np.arange(len(tokens)), x_h[tokens], ref_idx, ref_w, get_expert)
+    out = g["out"].float().numpy().astype(np.float64)[tokens]
+    rms = np.sqrt(np.mean(ref ** 2))
+    rel = 1e-4 if shape.dtype == "f32" else 2e-2
+    tol = rel * rms
+    if out_dtype == "bf16":
+        tol = tol + bf16_half_ulp(ref)
+    err = np.abs(out - ref)
+    assert np.all(err <= tol), "max err %.4g x RMS (limit %.1e)" % (np.max(err) / rms, rel)
+    return float(np.max(err) / rms), int((~keep).sum())
+
+
+# ---- whole layer, reduced shapes, every token -----------------------------------
+
+@pytest.mark.parametrize("name", sorted(TEST_SHAPES))
+def test_layer_reduced_shapes_all_tokens(name):
+    shape = TEST_SHAPES[name]
+    inp = make_inputs(shape, device="cuda")
+    for out_dtype in ("f32", "bf16") if shape.dtype == "bf16" else ("f32",):
+        g = run_layer(shape, inp, out_dtype)
+        err, excluded = check_layer(shape, inp, g, np.arange(shape.T), out_dtype)
+        print("%s out=%s: max err %.3g x RMS, %d tokens below the margin" % (name, out_dtype, err, excluded))
+
+
+# ---- whole layer at the workloads' full sizes, sampled tokens --------------------
+
+@pytest.mark.parametrize("name", ["deepseek_v3_decode", "deepseek_v3_prefill", "deepseek_v2", "mixtral_8x7b",
+                                  "tiny_mixtral_fp32"])
+def test_layer_full_size_sampled_tokens(name):
+    shape = CONFIGS[name]
+    inp = make_inputs(shape, device="cuda")
+    rng = np.random.default_rng(1234)
+    n = min(shape.T, 10)
+    tokens = np.unique(np.concatenate([[0, shape.T - 1], rng.choice(shape.T, n, replace=False)]))
+    outs = ("bf16", "f32") if shape.dtype == "bf16" else ("f32",)
+    for out_dtype in outs:
+        g = run_layer(shape, inp, out_dtype)
+        err, _ = check_layer(shape, inp, g, tokens, out_dtype)
+        print("%s out=%s: max err %.3g x RMS on %d tokens" % (name, out_dtype, err, len(tokens)))
+        # permutation invariants over all tokens
+        counts = g["counts"].numpy()
+        idx = g["idx"].numpy()
+        assert counts.sum() == (idx >= 0).sum()
+    del inp
+    torch.cuda.empty_cache()
+
+
+# ---- stages ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k,S,drop", [(1, 8, 2, 0, 0.0), (333, 160, 6, 2, 0.0), (2048, 256, 8, 1, 0.05),
+                                          (64, 8, 8, 0, 0.3), (4097, 16, 4, 3, 0.0)])
+def test_permute_bit_exact(T, E, k, S, drop):
+    from workloads import LayerShape
+    shape = LayerShape("p", T=T, H=256, E=E, S=S, k=k, I=128)
+    rng = np.random.default_rng(T * 7 + E)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[rng.random((T, k)) < drop] = -1
+    cfg = moe.make_config(shape)
+    counts, offsets, row_token, slot_row = moe.permute(cfg, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    oc, oo, ort, osr = oracle.permute(shape, idx)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    assert np.array_equal(offsets.cpu().numpy(), oo)
+    assert np.array_equal(row_token.cpu().numpy(), ort)
+    assert np.array_equal(slot_row.cpu().numpy(), osr)
+
+
+def test_expert_ffn_stage_rows():
+    shape = TEST_SHAPES["v2_small"]
+    inp = make_inputs(shape, device="cuda")
+    cfg = moe.make_config(shape)
+    T = shape.T
+    idx, _ = moe.route(cfg, T, inp["x"], inp["w_router"])
+    counts, offsets, row_token, slot_row = moe.permute(cfg, idx)
+    y = moe.expert_ffn(cfg, inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"], offsets, row_token)
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    rt = row_token.cpu().numpy()
+    x_h = to_oracle(inp["x"])
+    yh = y.float().cpu().numpy()
+    rng = np.random.default_rng(3)
+    for e in list(rng.choice(shape.E, 12, replace=False)) + [shape.E, shape.E + 1]:
+        if e < shape.E:
+            rows = np.arange(off[e], off[e + 1])
+        else:
+            rows = T * shape.k + (e - shape.E) * T + np.arange(T)
+        if rows.size == 0:
+            continue
+        ref = oracle.expert_rows(shape, x_h[rt[rows]], to_oracle(inp["w_gate"][e]), to_oracle(inp["w_up"][e]),
+                                 to_oracle(inp["w_down"][e]))
+        rms = np.sqrt(np.mean(ref ** 2))
+        err = np.max(np.abs(yh[rows] - ref))
+        assert err <= 2e-2 * rms + np.max(bf16_half_ulp(ref)), (e, err / rms)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_combine_stage(dtype):
+    from workloads import LayerShape
+    H = 256 if dtype == "bf16" else 64
+    shape = LayerShape("c", T=300, H=H, E=16, S=2, k=4, I=128, dtype=dtype)
+    rng = np.random.default_rng(4)
+    T, k, S = shape.T, shape.k, shape.S
+    idx = np.stack([rng.permutation(16)[:k] for _ in range(T)]).astype(np.int32)
+    idx[rng.random((T, k)) < 0.1] = -1
+    _, _, _, slot_row = oracle.permute(shape, idx)
+    w = rng.random((T, k)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    y = torch.from_numpy(rng.standard_normal((T * k + S * T, H)).astype(np.float32)).to(tdt)
+    cfg = moe.make_config(shape, out_dtype="f32")
+    out = moe.combine(cfg, T, y.cuda(), torch.from_numpy(slot_row).cuda(), torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.combine(shape, y.float().numpy().astype(np.float64), slot_row, w.astype(np.float64))
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-6, atol=1e-5)
+
+
+# ---- routing edge cases ------------------------------------------------------------
+
+def test_route_ties_and_sigmoid_near_ties_from_given_logits():
+    shape = TEST_SHAPES["v3_small"]
+    T, E = 256, shape.E
+    rng = np.random.default_rng(5)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[:32] = 0.25                                     # exact ties everywhere
+    # logits on consecutive fp32 values: sigmoid scores tie or differ by one ulp
+    base = np.float32(0.3)
+    L[32:128] = base + np.spacing(base) * rng.integers(0, 6, (96, E)).astype(np.float32)
+    L[128:160] = np.float32(90.0) * np.sign(rng.standard_normal((32, E))).astype(np.float32)  # clamp region
+    sb = np.zeros(E, np.float32)
+    sb[::3] = np.float32(2.0 ** -24)                  # biases at the resolution of the scores
+    cfg = moe.make_config(shape)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    Lg = torch.from_numpy(L).cuda()
+    idx, w = moe.route(cfg, T, logits_in=Lg, sel_bias=torch.from_numpy(sb).cuda(), expert_counts=counts)
+    torch.cuda.synchronize()
+    oidx, ow, _, oc = oracle.select(shape, L, sb)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
+    # softmax variant on the same logits
+    sm = TEST_SHAPES["v2_small"].with_(E=E, G=1, topk_group=1)
+    idx2, w2 = moe.route(moe.make_config(sm), T, logits_in=Lg)
+    torch.cuda.synchronize()
+    oidx2, ow2, _, _ = oracle.select(sm, L, None)
+    assert np.array_equal(idx2.cpu().numpy(), oidx2)
+    np.testing.assert_allclose(w2.cpu().numpy(), ow2, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("cf", [0.25, 1.25])
+def test_capacity_with_drops_and_overflow(cf):
+    shape = TEST_SHAPES["v3_decode_small"].with_(capacity_factor=cf)
+    inp = make_inputs(shape, device="cuda")
+    g = run_layer(shape, inp, "f32")
+    idx = g["idx"].numpy()
+    C = oracle.capacity(shape, shape.T)
+    assert g["counts"].numpy().max() <= C
+    if cf < 1:
+        assert (idx < 0).any()
+    check_layer(shape, inp, g, np.arange(shape.T), "f32")
+
+
+def test_all_tokens_to_one_expert():
+    shape = TEST_SHAPES["mixtral_small"].with_(T=700)
+    inp = make_inputs(shape, device="cuda")
+    lb = torch.zeros(shape.E, dtype=torch.float32, device="cuda")
+    lb[3] = 100.0
+    inp["logit_bias"] = lb
+    g = run_layer(shape, inp, "f32")
+    assert np.all(g["idx"].numpy()[:, 0] == 3)
+    assert g["counts"].numpy()[3] == shape.T
+    check_layer(shape, inp, g, np.arange(0, shape.T, 7), "f32")
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 65])
+def test_small_batches(T):
+    shape = TEST_SHAPES["v3_small"].with_(T=T)
+    inp = make_inputs(shape, device="cuda")
+    g = run_layer(shape, inp, "f32")
+    check_layer(shape, inp, g, np.arange(T), "f32")
+
+
+def test_top1_single_group():
+    shape = TEST_SHAPES["mixtral_small"].with_(name="top1", k=1, T=130)
+    inp = make_inputs(shape, device="cuda")
+    g = run_layer(shape, inp, "f32")
+    check_layer(shape, inp, g, np.arange(shape.T), "f32")
+
+
+def test_empty_batch_leaves_output_untouched():
+    shape = TEST_SHAPES["v3_small"]
+    inp = make_inputs(shape, device="cuda", T=1)
+    cfg = moe.make_config(shape, out_dtype="f32")
+    x0 = inp["x"][:0]
+    out = torch.full((0, shape.H), 7.0, device="cuda")
+    moe.forward(cfg, x0, inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], sel_bias=inp["sel_bias"],
+                out=out)
+    torch.cuda.synchronize()
+
+
+def test_deterministic_bitwise():
+    shape = TEST_SHAPES["v3_small"]
+    inp = make_inputs(shape, device="cuda")
+    a = run_layer(shape, inp, "bf16")
+    b = run_layer(shape, inp, "bf16")
+    for key in ("out", "idx", "w", "logits", "counts"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_timing_records_every_kernel():
+    shape = TEST_SHAPES["v3_small"]
+    inp = make_inputs(shape, device="cuda")
+    moe.timing_enable(64)
+    run_layer(shape, inp, "bf16")
+    t = moe.timing_read()
+    moe.timing_enable(0)
+    for name in ("router", "permute_count", "permute_scan", "permute_scatter", "schedule", "gateup_swiglu", "down",
+                 "combine"):
+        assert name in t and t[name][1] == 1 and t[name][0] > 0.0, name
+
+
+def test_native_library_is_the_one_loaded():
+    moe.lib()
+    maps = open("/proc/self/maps").read()
+    assert os.path.realpath(moe.LIB_PATH) in maps
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip

@@ -142,3 +142,28 @@ def test_empty_slots_are_skipped_and_bf16_inputs_are_exact():
         return bf16_bits_to_f64(wd[e]) @ (g / (1 + np.exp(-g)) * u)
     ref = np.stack([0.5 * ffn(1, 0), 0.25 * ffn(2, 1) + 0.75 * ffn(0, 1), np.zeros(8), ffn(3, 3) + 2 * ffn(1, 3)])
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_combine_over_permuted_rows_equals_token_forward():
+    # permute -> per-row experts -> combine must equal the per-token forward
+    rng = np.random.default_rng(8)
+    cfg = f32shape(T=11, H=8, I=16, E=5, S=2, k=2, scoring="sigmoid", scale=2.5, capacity_factor=0.8)
+    x = rng.standard_normal((11, 8)).astype(np.float32)
+    wr = rng.standard_normal((5, 8)).astype(np.float32)
+    wg = rng.standard_normal((7, 16, 8)).astype(np.float32)
+    wu = rng.standard_normal((7, 16, 8)).astype(np.float32)
+    wd = rng.standard_normal((7, 8, 16)).astype(np.float32)
+    res = oracle.forward(cfg, x, wr, wg, wu, wd)
+    assert np.any(res["idx"] < 0)  # capacity dropped something
+    counts, offsets, row_token, slot_row = oracle.permute(cfg, res["idx"])
+    T = 11
+    y = np.zeros((T * cfg.k + cfg.S * T, 8))
+    for e in range(cfg.E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if rows.size:
+            y[rows] = oracle.expert_rows(cfg, x[row_token[rows]], wg[e], wu[e], wd[e])
+    for s in range(cfg.S):
+        base = T * cfg.k + s * T
+        y[base:base + T] = oracle.expert_rows(cfg, x, wg[cfg.E + s], wu[cfg.E + s], wd[cfg.E + s])
+    out = oracle.combine(cfg, y, slot_row, res["w"])
+    np.testing.assert_allclose(out, res["out"], rtol=1e-12, atol=1e-12)
