@@ -70,13 +70,13 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * topk_group, moe_intermediate_size, routed_scaling_factor, scoring
  * function) plus the capacity factor of the capacity passage. */
 typedef struct moe_config {
-  int32_t hidden_size;           /* H; bf16 needs H % 256 == 0, f32 H % 4 == 0  */
-  int32_t n_routed_experts;      /* E, 1..1024                                    */
+  int32_t hidden_size;           /* H; bf16 needs H % 256 == 0, f32 H % 32 == 0 */
+  int32_t n_routed_experts;      /* E, 1..512                                     */
   int32_t n_shared_experts;      /* S >= 0, each shaped like a routed expert     */
   int32_t top_k;                 /* k, 1..min(E, 32)                              */
   int32_t n_group;               /* G >= 1, E % G == 0, E/G >= 2 when G > 1      */
   int32_t topk_group;            /* 1..G, top_k <= topk_group * E / G            */
-  int32_t moe_intermediate_size; /* I; bf16 needs I % 128 == 0, f32 I % 4 == 0  */
+  int32_t moe_intermediate_size; /* I; bf16 needs I % 128 == 0, f32 I % 32 == 0 */
   int32_t scoring;               /* moe_scoring                                   */
   int32_t norm_topk_prob;        /* 1: gates renormalised over the selection     */
   float routed_scaling_factor;   /* multiplies every routed gate (2.5 for V3)    */
@@ -132,17 +132,17 @@ moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx
  *   x              [T,H] input dtype
  *   w_gate, w_up   [E+S,I,H] input dtype;  w_down [E+S,H,I] input dtype
  *   expert_offsets [E+1], row_token [T*k+S*T] as written by moe_permute
- *   y_rows         [T*k+S*T, H] out, input dtype (bf16 rows for bf16 layers);
- *                  unused routed rows are left untouched
+ *   y_rows         [T*k+S*T, H] fp32 out; unused routed rows are left untouched
  * bf16 layers accumulate in fp32 on the matrix cores and round the SwiGLU
- * activation and y to bf16. */
+ * activation h to bf16 (the input of the down projection); expert outputs
+ * stay fp32 so the combine adds unrounded values. */
 moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const void* w_gate,
                           const void* w_up, const void* w_down, const int32_t* expert_offsets,
                           const int32_t* row_token, void* y_rows, void* ws, size_t ws_bytes, void* stream);
 
 /* Combine: out[t] = sum_j topk_w[t,j] * y_rows[slot_row[t,j]] (empty slots
  * skipped) + sum_s y_rows[T*k + s*T + t], accumulated in fp32 in that order.
- *   y_rows [T*k+S*T, H] input dtype; slot_row, topk_w [T,k]; out [T,H] out_dtype */
+ *   y_rows [T*k+S*T, H] fp32; slot_row, topk_w [T,k]; out [T,H] out_dtype */
 moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, const int32_t* slot_row,
                        const float* topk_w, void* out, void* stream);
 

@@ -149,11 +149,11 @@ def permute(cfg, topk_idx, ws=None, stream=None):
 
 
 def expert_ffn(cfg, x, w_gate, w_up, w_down, expert_offsets, row_token, y_rows=None, ws=None, stream=None):
-    """-> y_rows [T*k+S*T, H] (input dtype)"""
+    """-> y_rows [T*k+S*T, H] fp32"""
     T = x.shape[0]
     rows = T * cfg.top_k + cfg.n_shared_experts * T
     if y_rows is None:
-        y_rows = torch.empty((rows, cfg.hidden_size), dtype=x.dtype, device=x.device)
+        y_rows = torch.empty((rows, cfg.hidden_size), dtype=torch.float32, device=x.device)
     if ws is None:
         ws = workspace(cfg, T, x.device)
     _check(lib().moe_expert_ffn(ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(w_up), _p(w_down), _p(expert_offsets),

@@ -145,7 +145,7 @@ Layout layout_of(const Dims& d) {
   L.seg_len = take((E + S) * 4);
   L.mt_prefix = take((E + S + 1) * 4);
   L.h = take(rows * (size_t)d.I * d.esz);
-  L.y = take(rows * (size_t)d.H * d.esz);
+  L.y = take(rows * (size_t)d.H * 4);  // expert outputs are fp32
   L.total = off;
   return L;
 }

@@ -2,7 +2,7 @@
 //   out[t] = sum_j w[t,j] * y_rows[slot_row[t,j]] + sum_s y_rows[T*k + s*T + t]
 // ("15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the
 // router sketch's last line: weighted routed experts plus the shared expert).
-// One workgroup per token; 16-byte loads of y rows, fp32 accumulation in a
+// One workgroup per token; 16-byte loads of the fp32 expert rows, fp32 accumulation in a
 // fixed order (slots, then shared experts), so the result is deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -86,17 +86,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  (void)dtype;  // expert rows are fp32 for every input dtype
   dim3 grid(a.T), block(256);
-  if (dtype == 1) {
-    if (out_dtype == 1)
-      hipLaunchKernelGGL((combine_kernel<bf16, bf16>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((combine_kernel<bf16, float>), grid, block, 0, s, a);
-  } else {
-    if (out_dtype == 1)
-      hipLaunchKernelGGL((combine_kernel<float, bf16>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, a);
-  }
+  if (out_dtype == 1)
+    hipLaunchKernelGGL((combine_kernel<float, bf16>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, a);
   return hipGetLastError();
 }

@@ -11,7 +11,7 @@
 //            computes 128 h-columns of gate AND the same 128 of up, and the
 //            epilogue writes h = silu(g) * u (bf16) -- SwiGLU fused between
 //            the two projections;
-//   down     h rows are contiguous per expert; y_rows = h W_down^T (bf16).
+//   down     h rows are contiguous per expert; y_rows = h W_down^T (fp32).
 // bf16 tiles: 4 wavefronts, block tile BM x 256 (B rows) x 64 (K), each wave
 // WM x 128 on v_mfma_f32_32x32x16_bf16, operands double-buffered in LDS with
 // an XOR swizzle (conflict-free 16-byte reads), global loads for step k+1 in
@@ -160,15 +160,14 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
     __syncthreads();
   }
 
-  bf16* out = static_cast<bf16*>(a.c);
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = wr * WM + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (row >= rows) continue;
-      bf16* orow = out + (int64_t)(row0 + row) * a.N;
       if constexpr (GATEUP) {
+        bf16* orow = static_cast<bf16*>(a.c) + (int64_t)(row0 + row) * a.N;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const float g = acc[m][n][r], u = acc[m][n + 2][r];
@@ -176,8 +175,11 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
           orow[nt * 128 + wc * 64 + n * 32 + (lane & 31)] = (bf16)hv;
         }
       } else {
+        // expert outputs stay fp32 until the combine (bf16 here would put a
+        // second rounding of every expert output into the layer result)
+        float* orow = static_cast<float*>(a.c) + (int64_t)(row0 + row) * a.N;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = (bf16)acc[m][n][r];
+        for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = acc[m][n][r];
       }
     }
   }

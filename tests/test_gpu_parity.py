@@ -201,13 +201,15 @@ def test_combine_stage(dtype):
     idx[rng.random((T, k)) < 0.1] = -1
     _, _, _, slot_row = oracle.permute(shape, idx)
     w = rng.random((T, k)).astype(np.float32)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    y = torch.from_numpy(rng.standard_normal((T * k + S * T, H)).astype(np.float32)).to(tdt)
-    cfg = moe.make_config(shape, out_dtype="f32")
-    out = moe.combine(cfg, T, y.cuda(), torch.from_numpy(slot_row).cuda(), torch.from_numpy(w).cuda())
-    torch.cuda.synchronize()
-    ref = oracle.combine(shape, y.float().numpy().astype(np.float64), slot_row, w.astype(np.float64))
-    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-6, atol=1e-5)
+    y = torch.from_numpy(rng.standard_normal((T * k + S * T, H)).astype(np.float32))
+    for out_dtype in ("f32", "bf16"):
+        cfg = moe.make_config(shape, out_dtype=out_dtype)
+        out = moe.combine(cfg, T, y.cuda(), torch.from_numpy(slot_row).cuda(), torch.from_numpy(w).cuda())
+        torch.cuda.synchronize()
+        ref = oracle.combine(shape, y.numpy().astype(np.float64), slot_row, w.astype(np.float64))
+        o = out.float().cpu().numpy()
+        tol = 1e-5 + (bf16_half_ulp(ref) if out_dtype == "bf16" else 1e-6 * np.abs(ref))
+        assert np.all(np.abs(o - ref) <= tol)
 
 
 # ---- routing edge cases ------------------------------------------------------------
