@@ -24,9 +24,11 @@
 
 namespace {
 
-constexpr int kBK = 64;     // K elements per LDS stage
-constexpr int kBNB = 256;   // B rows per block tile
-constexpr int kWM = 128;    // rows per wavefront (bf16 path); BM = 2 * kWM
+constexpr int kBK = 64;                // K elements per LDS stage
+constexpr int kRowBytes = kBK * 2;     // bytes of one tile row in LDS
+constexpr int kStages = 2;             // LDS stages (2 x 64 KB)
+constexpr int kBNB = 256;              // B rows per block tile
+constexpr int kWM = 128;               // rows per wavefront (bf16 path); BM = 2 * kWM
 
 // Logical tile of this workgroup: XCD-contiguous order over [0, total).
 __device__ __forceinline__ bool tile_of_block(const GemmArgs& a, int BM, int& e, int& nt, int& row0, int& rows) {
@@ -53,65 +55,131 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& a, int BM, int& e,
   return true;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Wait until at most N of this wavefront's vector-memory operations (here the
+// global->LDS copies, which complete in order) are outstanding:
+// s_waitcnt vmcnt(N), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Tiles live in LDS as rows of 128 bytes (64 bf16 of K) whose eight 16-byte
+// chunks are permuted: chunk c of row r sits in slot c ^ sw(r) with
+// sw(r) = (r % 8) ^ ((r / 8) % 2).  Sixteen consecutive rows read at one chunk
+// then touch 16 distinct 16-byte bank groups, and so do any eight within a
+// 128-byte window: fragment reads are free of LDS bank conflicts.
+__device__ __forceinline__ int swz_of_row(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// One global->LDS copy of 16 bytes per lane: lane L reads src and writes LDS
+// bytes [dst + 16*L, dst + 16*L + 16) (dst is the same for the whole wave).
+__device__ __forceinline__ void copy16(const bf16* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
+
+// N copies: copy i reads base + off[i] and fills the 1 KB of LDS at dst + i*1024.
+template <int N>
+__device__ __forceinline__ void copy_rows(const bf16* base, const uint32_t (&off)[N], char* dst) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) copy16(base + off[i], dst + i * 1024);
+}
+
+// MFMA operand fragments of one 16-wide K step from the swizzled LDS tiles.
+template <int MB>
+__device__ __forceinline__ void load_frags(const char* sa, int arow, const int (&brow)[4], int slot, int a_bytes,
+                                           bf16x8 (&fa)[MB], bf16x8 (&fb)[4]) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m) fa[m] = *reinterpret_cast<const bf16x8*>(sa + arow + m * 32 * kRowBytes + slot);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) fb[n] = *reinterpret_cast<const bf16x8*>(sa + a_bytes + brow[n] + slot);
+}
+
+template <int MB>
+__device__ __forceinline__ void mfma_step(const bf16x8 (&fa)[MB], const bf16x8 (&fb)[4], f32x16 (&acc)[MB][4]) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+}
+
+// Interleave the MFMAs and LDS reads of one 16-wide K step: one read after
+// each of the first MB+4 MFMAs, so the reads land while the rest execute.
+template <int MB>
+__device__ __forceinline__ void interleave_reads() {
+#pragma unroll
+  for (int i = 0; i < MB + 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, MB * 4 - (MB + 4), 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Pipeline per K step of 64 (two LDS stages): the four 16-wide sub-steps run
+// their MFMAs while the next sub-step's fragments are read.  The one barrier
+// per step sits before the last sub-step, once every wave has read its last
+// fragments of the current stage: the stage is then refilled with step kt+2
+// while the last MFMAs run and step kt+1's first fragments are read, so the
+// matrix cores do not wait for the barrier or for the first LDS reads.
 template <int WM, bool GATEUP>
 __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
   constexpr int BM = 2 * WM;
   constexpr int MB = WM / 32;
-  constexpr int A_LOADS = BM * 8 / 256;
-  constexpr int B_LOADS = kBNB * 8 / 256;
-  constexpr int STAGE = (BM + kBNB) * kBK * 2;  // bytes
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+  constexpr int A_BYTES = BM * kRowBytes;
+  constexpr int STAGE = A_BYTES + kBNB * kRowBytes;
+  constexpr int A_PER_WAVE = BM / 8 / 4;    // 8-row groups of A each wave copies
+  constexpr int B_PER_WAVE = kBNB / 8 / 4;  // 8-row groups of B each wave copies
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * STAGE];
 
   int e, nt, row0, rows;
   if (!tile_of_block(a, BM, e, nt, row0, rows)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int ch = tid & 7, rbase = tid >> 3;
   const int K = a.K;
+  // a copy writes 64 lanes x 16 bytes = 8 rows of 128 bytes: lane L lands in
+  // row L/8 of its group, slot L%8, so it fetches chunk (L%8) ^ sw(row)
+  const int lrow = lane >> 3;
 
-  const bf16* aptr[A_LOADS];
+  const bf16* abase;
+  uint32_t aoff[A_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int rr = min(rbase + 32 * i, rows - 1);
-    if constexpr (GATEUP) {
-      const int tok = a.row_token[row0 + rr];
-      aptr[i] = static_cast<const bf16*>(a.a) + (int64_t)tok * K + ch * 8;
-    } else {
-      aptr[i] = static_cast<const bf16*>(a.a) + (int64_t)(row0 + rr) * K + ch * 8;
+  for (int i = 0; i < A_PER_WAVE; ++i) {
+    const int r = (wave * A_PER_WAVE + i) * 8 + lrow;
+    const int rr = min(r, rows - 1);
+    const int chunk = (lane & 7) ^ swz_of_row(r);
+    if constexpr (GATEUP)
+      aoff[i] = (uint32_t)a.row_token[row0 + rr] * (uint32_t)K + chunk * 8;
+    else
+      aoff[i] = (uint32_t)rr * (uint32_t)K + chunk * 8;
+  }
+  if constexpr (GATEUP)
+    abase = static_cast<const bf16*>(a.a);
+  else
+    abase = static_cast<const bf16*>(a.a) + (int64_t)row0 * K;
+
+  const bf16* bbase;
+  uint32_t boff[B_PER_WAVE];
+  if constexpr (GATEUP) {
+    // waves 0-1 copy the 128 gate rows, waves 2-3 the 128 up rows
+    bbase = static_cast<const bf16*>(wave < 2 ? a.b0 : a.b1) + ((int64_t)e * a.N + nt * 128) * K;
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int rb = ((wave & 1) * B_PER_WAVE + i) * 8 + lrow;
+      boff[i] = (uint32_t)rb * (uint32_t)K + ((lane & 7) ^ swz_of_row(rb)) * 8;
+    }
+  } else {
+    bbase = static_cast<const bf16*>(a.b0) + ((int64_t)e * a.N + nt * kBNB) * K;
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int rb = (wave * B_PER_WAVE + i) * 8 + lrow;
+      boff[i] = (uint32_t)rb * (uint32_t)K + ((lane & 7) ^ swz_of_row(rb)) * 8;
     }
   }
-  const bf16* bptr[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int rb = rbase + 32 * i;
-    if constexpr (GATEUP) {
-      const int n = nt * 128 + (rb & 127);
-      const bf16* mat = static_cast<const bf16*>(rb < 128 ? a.b0 : a.b1);
-      bptr[i] = mat + ((int64_t)e * a.N + n) * K + ch * 8;
-    } else {
-      const int n = nt * kBNB + rb;
-      bptr[i] = static_cast<const bf16*>(a.b0) + ((int64_t)e * a.N + n) * K + ch * 8;
-    }
-  }
-
-  u32x4 ra[A_LOADS], rb[B_LOADS];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + k0);
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + k0);
-  };
-  auto lstore = [&](int stage) {
-    char* sa = lds + stage * STAGE;
-    char* sb = sa + BM * kBK * 2;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<u32x4*>(sa + swz(rbase + 32 * i, ch)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<u32x4*>(sb + swz(rbase + 32 * i, ch)) = rb[i];
-  };
+  char* const a_dst = lds + wave * A_PER_WAVE * 1024;
+  char* const b_dst = lds + A_BYTES + wave * B_PER_WAVE * 1024;
 
   f32x16 acc[MB][4];
 #pragma unroll
@@ -122,42 +190,65 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
 
   const int wr = wave & 1, wc = wave >> 1;
+  // fragment rows: A row wr*WM + m*32 + lane%32, B row brow[n] + lane%32; all
+  // are congruent to lane mod 16, so the swizzled slot only depends on lane
+  const int arow = (wr * WM + (lane & 31)) * kRowBytes;
   int brow[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     if constexpr (GATEUP)
-      brow[n] = (n < 2 ? wc * 64 + n * 32 : 128 + wc * 64 + (n - 2) * 32) + (lane & 31);
+      brow[n] = ((n < 2 ? wc * 64 + n * 32 : 128 + wc * 64 + (n - 2) * 32) + (lane & 31)) * kRowBytes;
     else
-      brow[n] = wc * 128 + n * 32 + (lane & 31);
+      brow[n] = (wc * 128 + n * 32 + (lane & 31)) * kRowBytes;
   }
+  int slot[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) slot[kk] = ((kk * 2 + (lane >> 5)) ^ swz_of_row(lane & 15)) << 4;
 
   const int nk = K / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // prologue: steps 0 and 1 in flight, wait for step 0
+  copy_rows<A_PER_WAVE>(abase, aoff, a_dst);
+  copy_rows<B_PER_WAVE>(bbase, boff, b_dst);
+  if (nk > 1) {
+    copy_rows<A_PER_WAVE>(abase + kBK, aoff, a_dst + STAGE);
+    copy_rows<B_PER_WAVE>(bbase + kBK, boff, b_dst + STAGE);
+    wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
+  } else {
+    wait_vmem_upto<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+
+  bf16x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
+  load_frags<MB>(lds, arow, brow, slot[0], A_BYTES, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
-    const char* sa = lds + (kt & 1) * STAGE;
-    const char* sb = sa + BM * kBK * 2;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int chunk = kk * 2 + (lane >> 5);
-      bf16x8 af[MB], bfv[4];
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const int row = wr * WM + m * 32 + (lane & 31);
-        af[m] = *reinterpret_cast<const bf16x8*>(sa + swz(row, chunk));
-      }
-#pragma unroll
-      for (int n = 0; n < 4; ++n) bfv[n] = *reinterpret_cast<const bf16x8*>(sb + swz(brow[n], chunk));
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfv[n], acc[m][n], 0, 0, 0);
+    const int cur = kt & 1;
+    const char* sa = lds + cur * STAGE;
+    load_frags<MB>(sa, arow, brow, slot[1], A_BYTES, fa1, fb1);
+    mfma_step<MB>(fa0, fb0, acc);
+    interleave_reads<MB>();
+    load_frags<MB>(sa, arow, brow, slot[2], A_BYTES, fa0, fb0);
+    mfma_step<MB>(fa1, fb1, acc);
+    interleave_reads<MB>();
+    load_frags<MB>(sa, arow, brow, slot[3], A_BYTES, fa1, fb1);
+    mfma_step<MB>(fa0, fb0, acc);
+    interleave_reads<MB>();
+    // this wave's reads of the current stage are done and step kt+1 has
+    // landed (it is the only copy in flight); after the barrier every wave
+    // is past the current stage
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    wait_vmem_upto<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 2 < nk) {
+      const int k2 = (kt + 2) * kBK;
+      copy_rows<A_PER_WAVE>(abase + k2, aoff, a_dst + cur * STAGE);
+      copy_rows<B_PER_WAVE>(bbase + k2, boff, b_dst + cur * STAGE);
     }
-    if (kt + 1 < nk) lstore((kt + 1) & 1);
-    __syncthreads();
+    // last sub-step; step kt+1's first fragments are read meanwhile (after the
+    // last step this reads a stage that is never used: harmless)
+    load_frags<MB>(lds + (cur ^ 1) * STAGE, arow, brow, slot[0], A_BYTES, fa0, fb0);
+    mfma_step<MB>(fa1, fb1, acc);
+    interleave_reads<MB>();
   }
 
 #pragma unroll

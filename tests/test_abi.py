@@ -123,3 +123,11 @@ def test_product_and_oracle_are_separate():
     assert "#include \"" not in osrc and "moe.h" not in osrc
     opy = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
     assert "routing_expert_ffn_amd" not in opy
+
+
+def test_every_kernel_launch_stub_is_defined():
+    """A kernel whose host-side stub was dropped by the compiler leaves an
+    undefined __device_stub__ symbol and the library fails to load on a GPU
+    host; catch it at build time."""
+    out = subprocess.run(["nm", "-u", moe.LIB_PATH], capture_output=True, text=True).stdout
+    assert "__device_stub__" not in out
