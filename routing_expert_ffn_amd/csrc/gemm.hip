@@ -27,6 +27,7 @@ namespace {
 constexpr int kBK = 64;                // K elements per LDS stage
 constexpr int kRowBytes = kBK * 2;     // bytes of one tile row in LDS
 constexpr int kStages = 2;             // LDS stages (2 x 64 KB)
+constexpr bool kPrefetchL2 = false;    // warm L2 two steps ahead of each copy (measured: no gain)
 constexpr int kBNB = 256;              // B rows per block tile
 constexpr int kWM = 128;               // rows per wavefront (bf16 path); BM = 2 * kWM
 
@@ -123,18 +124,23 @@ __device__ __forceinline__ void interleave_reads() {
 // fragments of the current stage: the stage is then refilled with step kt+2
 // while the last MFMAs run and step kt+1's first fragments are read, so the
 // matrix cores do not wait for the barrier or for the first LDS reads.
+// LDS of one stage: the A tile region is sized for full row tiles (2 * kWM
+// rows); half tiles use its first half.
+constexpr int kABytes = 2 * kWM * kRowBytes;
+constexpr int kStageBytes = kABytes + kBNB * kRowBytes;
+
+// One output tile: rows [row0, row0 + rows) of expert e, column tile nt.  WM
+// is the row count per wavefront: kWM for a full tile (2*kWM rows), kWM/2 for
+// a tile of at most kWM rows (an expert's last, short row tile), which then
+// costs half the MFMAs instead of computing padding.
 template <int WM, bool GATEUP>
-__global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, int nt, int row0, int rows) {
   constexpr int BM = 2 * WM;
   constexpr int MB = WM / 32;
-  constexpr int A_BYTES = BM * kRowBytes;
-  constexpr int STAGE = A_BYTES + kBNB * kRowBytes;
+  constexpr int A_BYTES = kABytes;
+  constexpr int STAGE = kStageBytes;
   constexpr int A_PER_WAVE = BM / 8 / 4;    // 8-row groups of A each wave copies
   constexpr int B_PER_WAVE = kBNB / 8 / 4;  // 8-row groups of B each wave copies
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * STAGE];
-
-  int e, nt, row0, rows;
-  if (!tile_of_block(a, BM, e, nt, row0, rows)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -180,6 +186,22 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
   }
   char* const a_dst = lds + wave * A_PER_WAVE * 1024;
   char* const b_dst = lds + A_BYTES + wave * B_PER_WAVE * 1024;
+  // L2 warm-up: two steps before a stage is copied, each lane touches one
+  // 16-byte piece of one A row and one B row of it (64 rows per wave), so the
+  // copy itself hits L2; the pieces land in a per-wave scratch kilobyte.
+  char* const junk = lds + kStages * STAGE + wave * 1024;
+  uint32_t pa_off, pb_off;
+  {
+    const int r = wave * 64 + lane;
+    const int rr = min(r, rows - 1);
+    if constexpr (GATEUP) {
+      pa_off = (uint32_t)a.row_token[row0 + rr] * (uint32_t)K;
+      pb_off = (uint32_t)((wave & 1) * 64 + lane) * (uint32_t)K;
+    } else {
+      pa_off = (uint32_t)rr * (uint32_t)K;
+      pb_off = (uint32_t)r * (uint32_t)K;
+    }
+  }
 
   f32x16 acc[MB][4];
 #pragma unroll
@@ -206,16 +228,23 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
   for (int kk = 0; kk < 4; ++kk) slot[kk] = ((kk * 2 + (lane >> 5)) ^ swz_of_row(lane & 15)) << 4;
 
   const int nk = K / kBK;
-  // prologue: steps 0 and 1 in flight, wait for step 0
+  // prologue: steps 0 and 1 in flight (and step 3 warmed), wait for step 0
   copy_rows<A_PER_WAVE>(abase, aoff, a_dst);
   copy_rows<B_PER_WAVE>(bbase, boff, b_dst);
   if (nk > 1) {
     copy_rows<A_PER_WAVE>(abase + kBK, aoff, a_dst + STAGE);
     copy_rows<B_PER_WAVE>(bbase + kBK, boff, b_dst + STAGE);
-    wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
-  } else {
-    wait_vmem_upto<0>();
   }
+  if (kPrefetchL2 && nk > 3) {
+    copy16(abase + 3 * kBK + pa_off, junk);
+    copy16(bbase + 3 * kBK + pb_off, junk);
+  }
+  if (nk > 3)
+    wait_vmem_upto<A_PER_WAVE + B_PER_WAVE + (kPrefetchL2 ? 2 : 0)>();
+  else if (nk > 1)
+    wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
+  else
+    wait_vmem_upto<0>();
   __builtin_amdgcn_s_barrier();
 
   bf16x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
@@ -236,19 +265,38 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
     // landed (it is the only copy in flight); after the barrier every wave
     // is past the current stage
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    wait_vmem_upto<0>();
+    // only the warm-up of step kt+3 was issued after step kt+1's copies
+    if (kPrefetchL2 && kt + 3 < nk)
+      wait_vmem_upto<2>();
+    else
+      wait_vmem_upto<0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 2 < nk) {
-      const int k2 = (kt + 2) * kBK;
+    if (kPrefetchL2 && kt + 4 < nk) {
+      const int k4 = (kt + 4) * kBK;
+      copy16(abase + k4 + pa_off, junk);
+      copy16(bbase + k4 + pb_off, junk);
+    }
+    // last sub-step: the freed stage is refilled with step kt+2 (the last two
+    // steps re-copy step nk-1, which keeps this region branch-free), step
+    // kt+1's first fragments are read (after the last step: a stage that is
+    // never used, harmless), and both interleave with the MFMAs
+    {
+      const int k2 = min(kt + 2, nk - 1) * kBK;
       copy_rows<A_PER_WAVE>(abase + k2, aoff, a_dst + cur * STAGE);
       copy_rows<B_PER_WAVE>(bbase + k2, boff, b_dst + cur * STAGE);
     }
-    // last sub-step; step kt+1's first fragments are read meanwhile (after the
-    // last step this reads a stage that is never used: harmless)
     load_frags<MB>(lds + (cur ^ 1) * STAGE, arow, brow, slot[0], A_BYTES, fa0, fb0);
     mfma_step<MB>(fa1, fb1, acc);
-    interleave_reads<MB>();
+#pragma unroll
+    for (int i = 0; i < MB + 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global->LDS copy
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global->LDS copy
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MB * 4 - (MB + 4), 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
 #pragma unroll
@@ -274,6 +322,17 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
       }
     }
   }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes + (kPrefetchL2 ? 4096 : 0)];
+  int e, nt, row0, rows;
+  if (!tile_of_block(a, 2 * kWM, e, nt, row0, rows)) return;
+  if (rows > kWM)
+    gemm_tile<kWM, GATEUP>(a, lds, e, nt, row0, rows);
+  else
+    gemm_tile<kWM / 2, GATEUP>(a, lds, e, nt, row0, rows);
 }
 
 // fp32 layers: one wavefront per 32 x 32 output tile on v_mfma_f32_32x32x2_f32,
@@ -370,7 +429,7 @@ hipError_t launch_gateup(const GemmArgs& a, int dtype, int64_t mtile_bound, hipS
   const int64_t grid = mtile_bound * a.n_tiles;
   if (grid <= 0) return hipSuccess;
   if (dtype == 1)
-    hipLaunchKernelGGL((expert_gemm_bf16<kWM, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<true>), dim3((unsigned)grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((expert_gemm_f32<true>), dim3((unsigned)grid), dim3(64), 0, s, a);
   return hipGetLastError();
@@ -380,7 +439,7 @@ hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStr
   const int64_t grid = mtile_bound * a.n_tiles;
   if (grid <= 0) return hipSuccess;
   if (dtype == 1)
-    hipLaunchKernelGGL((expert_gemm_bf16<kWM, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((expert_gemm_f32<false>), dim3((unsigned)grid), dim3(64), 0, s, a);
   return hipGetLastError();

@@ -322,3 +322,35 @@ def test_native_library_is_the_one_loaded():
     assert os.path.realpath(moe.LIB_PATH) in maps
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+def test_expert_ffn_row_tile_boundaries():
+    """Experts whose row counts sit on and around the row-tile sizes (full
+    256-row tiles and the half tiles used for short remainders)."""
+    from workloads import LayerShape
+    counts = [128, 256, 129, 1, 0, 127, 255, 257, 384, 385]
+    E = len(counts)
+    T = max(counts)
+    shape = LayerShape("tb", T=T, H=256, E=E, S=1, k=E, I=256)
+    # token t is routed to every expert e with t < counts[e] (slots in expert order)
+    idx = np.full((T, E), -1, np.int32)
+    for t in range(T):
+        es = [e for e in range(E) if t < counts[e]]
+        idx[t, :len(es)] = es
+    inp = make_inputs(shape, device="cuda")
+    cfg = moe.make_config(shape)
+    c, off, rt, sr = moe.permute(cfg, torch.from_numpy(idx).cuda())
+    y = moe.expert_ffn(cfg, inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"], off, rt)
+    torch.cuda.synchronize()
+    assert c.cpu().numpy().tolist() == counts
+    offh, rth, yh = off.cpu().numpy(), rt.cpu().numpy(), y.cpu().numpy()
+    x_h = to_oracle(inp["x"])
+    for e in list(range(E)) + [E]:
+        rows = np.arange(offh[e], offh[e + 1]) if e < E else T * E + np.arange(T)
+        if rows.size == 0:
+            continue
+        ref = oracle.expert_rows(shape, x_h[rth[rows]], to_oracle(inp["w_gate"][e]), to_oracle(inp["w_up"][e]),
+                                 to_oracle(inp["w_down"][e]))
+        rms = np.sqrt(np.mean(ref ** 2))
+        err = np.max(np.abs(yh[rows] - ref))
+        assert err <= 2e-2 * rms, (e, counts[e] if e < E else T, err / rms)
