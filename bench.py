@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--workload", default="deepseek_v3_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="copy 1 GiB device-to-device 3 times first (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -123,6 +125,15 @@ def main():
     out = torch.empty((T, shape.H), dtype=torch.bfloat16, device=dev)
     idx = torch.empty((T, shape.k), dtype=torch.int32, device=dev)
     counts = torch.empty((shape.E,), dtype=torch.int32, device=dev)
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration: 3 device copies of 1 GiB")
 
     def step():
         moe.forward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
