@@ -117,7 +117,7 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
 
 struct Layout {
   size_t logits, cand, idx, w, counts, offsets, slot_row, row_token, chunk_cnt, chunk_base, seg_start, seg_len,
-      mt_prefix, h, y, total;
+      f_prefix, h_prefix, h, y, total;
 };
 
 Layout layout_of(const Dims& d) {
@@ -143,7 +143,8 @@ Layout layout_of(const Dims& d) {
   L.chunk_base = take(nchunks * E * 4);
   L.seg_start = take((E + S) * 4);
   L.seg_len = take((E + S) * 4);
-  L.mt_prefix = take((E + S + 1) * 4);
+  L.f_prefix = take((E + S + 1) * 4);
+  L.h_prefix = take((E + S + 1) * 4);
   L.h = take(rows * (size_t)d.I * d.esz);
   L.y = take(rows * (size_t)d.H * 4);  // expert outputs are fp32
   L.total = off;
@@ -271,10 +272,12 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   sa.S = d.S;
   sa.k = d.k;
   sa.BM = BM;
+  sa.half_rows = gemm_half_rows(d.dtype);
   sa.offsets = offsets;
   sa.seg_start = at<int32_t>(ws, L.seg_start);
   sa.seg_len = at<int32_t>(ws, L.seg_len);
-  sa.mt_prefix = at<int32_t>(ws, L.mt_prefix);
+  sa.f_prefix = at<int32_t>(ws, L.f_prefix);
+  sa.h_prefix = at<int32_t>(ws, L.h_prefix);
   hipError_t e = timed(K_SCHEDULE, s, [&] { return launch_schedule(sa, s); });
   if (e != hipSuccess) return hip_fail(e, "schedule launch");
   const int64_t bound = gemm_mtile_bound((int)d.T, d.E, d.S, d.k, BM);
@@ -282,7 +285,8 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   g.n_exp = d.E + d.S;
   g.seg_start = sa.seg_start;
   g.seg_len = sa.seg_len;
-  g.mt_prefix = sa.mt_prefix;
+  g.f_prefix = sa.f_prefix;
+  g.h_prefix = sa.h_prefix;
   g.row_token = row_token;
   void* h = at<void>(ws, L.h);
   // gate/up + SwiGLU

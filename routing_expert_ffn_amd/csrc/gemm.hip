@@ -15,10 +15,10 @@
 // bf16 tiles: 4 wavefronts, block tile BM x 256 (B rows) x 64 (K), each wave
 // WM x 128 on v_mfma_f32_32x32x16_bf16, operands double-buffered in LDS with
 // an XOR swizzle (conflict-free 16-byte reads), global loads for step k+1 in
-// flight while step k computes.  Tiles are mapped so that each XCD (one L2)
-// walks a contiguous range of logical tiles, row tiles of one (expert, column
-// tile) being adjacent: the weight tile is fetched once per XCD and reused
-// from L2 by the expert's row tiles.
+// flight while step k computes.  Work items (see work_of_block) are ordered
+// so that each XCD (one L2) walks a contiguous range in which the row tiles
+// sharing a weight tile, and the column tiles sharing an input row tile, run
+// side by side and re-read the shared operand from L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,33 +26,83 @@ namespace {
 
 constexpr int kBK = 64;                // K elements per LDS stage
 constexpr int kRowBytes = kBK * 2;     // bytes of one tile row in LDS
-constexpr int kStages = 2;             // LDS stages (2 x 64 KB)
-constexpr bool kPrefetchL2 = false;    // warm L2 two steps ahead of each copy (measured: no gain)
 constexpr int kBNB = 256;              // B rows per block tile
 constexpr int kWM = 128;               // rows per wavefront (bf16 path); BM = 2 * kWM
+// LDS: two A stages (input rows) and three B stages (weight rows), 32 KB
+// each, 160 KB in all.  A row tile is shared by all column tiles of an
+// expert and mostly hits L2; a weight tile is shared by the expert's few row
+// tiles and more often comes from HBM, so weights are copied two steps ahead
+// of use and inputs one step ahead.
+constexpr int kAStage = 2 * kWM * kRowBytes;
+constexpr int kBStage = kBNB * kRowBytes;
+constexpr int kAStages = 2, kBStages = 3;
+constexpr int kLdsBytes = kAStages * kAStage + kBStages * kBStage;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 
-// Logical tile of this workgroup: XCD-contiguous order over [0, total).
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& a, int BM, int& e, int& nt, int& row0, int& rows) {
-  const int total = a.mt_prefix[a.n_exp] * a.n_tiles;
+constexpr int kGroup = 4;             // full row tiles of an expert walked together
+
+// Work item of one workgroup.  The items of an expert are ordered as: groups
+// of up to kGroup full row tiles; inside a group, column-tile pairs (2p, 2p+1),
+// first every full row tile of the group at column 2p, then at 2p+1, then --
+// in the expert's last group only -- one item that runs the expert's short
+// last row tile (at most half_rows rows, half the MFMA work) at both columns.
+// Every item then takes about one full tile's time, items that share a weight
+// tile or a row tile of the input are close together, and each XCD (one L2)
+// walks a contiguous range of items, so neighbours run at the same time and
+// re-read shared operands from L2.
+struct Work {
+  int e, nt, row0, rows;
+  bool pair;  // short row tile at columns nt and nt + 1 (when nt + 1 exists)
+};
+
+__device__ __forceinline__ int items_before(const GemmArgs& a, int e, int np) {
+  return a.f_prefix[e] * a.n_tiles + a.h_prefix[e] * np;
+}
+
+__device__ __forceinline__ bool work_of_block(const GemmArgs& a, int BM, Work& w) {
+  const int ntn = a.n_tiles;
+  const int np = (ntn + 1) >> 1;
+  const int total = items_before(a, a.n_exp, np);
   const int bid = blockIdx.x;
   if (bid >= total) return false;
   const int xcd = bid & 7, q = total >> 3, r = total & 7;
   const int L = xcd * q + min(xcd, r) + (bid >> 3);
+  // largest e with items_before(e) <= L (experts without items are skipped)
   int lo = 0, hi = a.n_exp;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.mt_prefix[mid] * a.n_tiles <= L)
+    if (items_before(a, mid, np) <= L)
       lo = mid;
     else
       hi = mid;
   }
-  e = lo;
-  const int local = L - a.mt_prefix[e] * a.n_tiles;
-  const int me = a.mt_prefix[e + 1] - a.mt_prefix[e];
-  nt = local / me;
-  const int mt = local - nt * me;
-  row0 = a.seg_start[e] + mt * BM;
-  rows = min(BM, a.seg_len[e] - mt * BM);
+  const int e = lo;
+  int i = L - items_before(a, e, np);
+  const int F = a.f_prefix[e + 1] - a.f_prefix[e];
+  const int Hs = a.h_prefix[e + 1] - a.h_prefix[e];
+  const int nfg = max(1, (F + kGroup - 1) / kGroup);
+  const int g = min(i / (kGroup * ntn), nfg - 1);
+  i -= g * kGroup * ntn;
+  const int f = min(kGroup, F - g * kGroup);  // >= 1, or 0 when F == 0 (then Hs == 1)
+  const int h = g == nfg - 1 ? Hs : 0;
+  const int bs = 2 * f + h;                   // items per column pair
+  const int p = min(i / bs, np - 1);
+  const int j = i - p * bs;
+  const int ncols = 2 * p + 1 < ntn ? 2 : 1;
+  const int len = a.seg_len[e];
+  w.e = e;
+  if (j < f * ncols) {
+    const int mt = g * kGroup + j % f;
+    w.nt = 2 * p + j / f;
+    w.row0 = a.seg_start[e] + mt * BM;
+    w.rows = min(BM, len - mt * BM);
+    w.pair = false;
+  } else {
+    w.nt = 2 * p;
+    w.row0 = a.seg_start[e] + F * BM;
+    w.rows = len - F * BM;
+    w.pair = true;
+  }
   return true;
 }
 
@@ -80,21 +130,24 @@ __device__ __forceinline__ void copy16(const bf16* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
 }
 
-// N copies: copy i reads base + off[i] and fills the 1 KB of LDS at dst + i*1024.
-template <int N>
-__device__ __forceinline__ void copy_rows(const bf16* base, const uint32_t (&off)[N], char* dst) {
+// Copies I0 .. I0+N-1 of a wave's group: copy i reads base + off[i] and
+// fills the 1 KB of LDS at dst + i*1024.
+template <int I0, int N, int M>
+__device__ __forceinline__ void copy_rows(const bf16* base, const uint32_t (&off)[M], char* dst) {
+  static_assert(I0 + N <= M, "copy range");
 #pragma unroll
-  for (int i = 0; i < N; ++i) copy16(base + off[i], dst + i * 1024);
+  for (int i = I0; i < I0 + N; ++i) copy16(base + off[i], dst + i * 1024);
 }
 
-// MFMA operand fragments of one 16-wide K step from the swizzled LDS tiles.
+// MFMA operand fragments of one 16-wide K step from the swizzled LDS tiles
+// (sa: A stage, sb: B stage).
 template <int MB>
-__device__ __forceinline__ void load_frags(const char* sa, int arow, const int (&brow)[4], int slot, int a_bytes,
+__device__ __forceinline__ void load_frags(const char* sa, const char* sb, int arow, const int (&brow)[4], int slot,
                                            bf16x8 (&fa)[MB], bf16x8 (&fb)[4]) {
 #pragma unroll
   for (int m = 0; m < MB; ++m) fa[m] = *reinterpret_cast<const bf16x8*>(sa + arow + m * 32 * kRowBytes + slot);
 #pragma unroll
-  for (int n = 0; n < 4; ++n) fb[n] = *reinterpret_cast<const bf16x8*>(sa + a_bytes + brow[n] + slot);
+  for (int n = 0; n < 4; ++n) fb[n] = *reinterpret_cast<const bf16x8*>(sb + brow[n] + slot);
 }
 
 template <int MB>
@@ -105,29 +158,38 @@ __device__ __forceinline__ void mfma_step(const bf16x8 (&fa)[MB], const bf16x8 (
     for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
 }
 
-// Interleave the MFMAs and LDS reads of one 16-wide K step: one read after
-// each of the first MB+4 MFMAs, so the reads land while the rest execute.
-template <int MB>
+// Interleave one 16-wide K step: a fragment read after each of the first
+// MB+4 MFMAs, so the reads land while the rest execute, then the NC
+// global->LDS copies of the sub-step one per MFMA (the compiler keeps LDS
+// reads and copies in program order, so the reads are written first).  The
+// copy stream is spread over the whole K step: bunched, it queues behind the
+// address unit and stalls the wave's in-order issue, MFMAs included.
+template <int MB, int NC>
 __device__ __forceinline__ void interleave_reads() {
+  constexpr int NR = MB + 4, NM = MB * 4 - NR;  // MFMAs left after the reads
 #pragma unroll
-  for (int i = 0; i < MB + 4; ++i) {
+  for (int i = 0; i < NR; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, MB * 4 - (MB + 4), 0);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);              // 1 copy
+  }
+  if (NM > NC) __builtin_amdgcn_sched_group_barrier(0x008, NM - NC, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Pipeline per K step of 64 (two LDS stages): the four 16-wide sub-steps run
-// their MFMAs while the next sub-step's fragments are read.  The one barrier
-// per step sits before the last sub-step, once every wave has read its last
-// fragments of the current stage: the stage is then refilled with step kt+2
-// while the last MFMAs run and step kt+1's first fragments are read, so the
-// matrix cores do not wait for the barrier or for the first LDS reads.
-// LDS of one stage: the A tile region is sized for full row tiles (2 * kWM
-// rows); half tiles use its first half.
-constexpr int kABytes = 2 * kWM * kRowBytes;
-constexpr int kStageBytes = kABytes + kBNB * kRowBytes;
+// Pipeline per K step of 64: the four 16-wide sub-steps run their MFMAs
+// while the next sub-step's fragments are read.  The one barrier per step
+// sits before the last sub-step, once every wave has read its last fragments
+// of the current stages, so the matrix cores wait neither for the barrier nor
+// for the first LDS reads of the next step.  The copies refilling the freed
+// stages are spread over four sub-steps: half of A of step kt+2 in the last
+// sub-step of step kt, the other half in sub-step 0 of step kt+1, then B of
+// step kt+3 in its sub-steps 1 and 2 (B has three stages).  Before the
+// barrier of step kt a wave waits until only B of step kt+2 is in flight.
 
 // One output tile: rows [row0, row0 + rows) of expert e, column tile nt.  WM
 // is the row count per wavefront: kWM for a full tile (2*kWM rows), kWM/2 for
@@ -137,8 +199,6 @@ template <int WM, bool GATEUP>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, int nt, int row0, int rows) {
   constexpr int BM = 2 * WM;
   constexpr int MB = WM / 32;
-  constexpr int A_BYTES = kABytes;
-  constexpr int STAGE = kStageBytes;
   constexpr int A_PER_WAVE = BM / 8 / 4;    // 8-row groups of A each wave copies
   constexpr int B_PER_WAVE = kBNB / 8 / 4;  // 8-row groups of B each wave copies
 
@@ -184,24 +244,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
       boff[i] = (uint32_t)rb * (uint32_t)K + ((lane & 7) ^ swz_of_row(rb)) * 8;
     }
   }
+  char* const b_lds = lds + kAStages * kAStage;
   char* const a_dst = lds + wave * A_PER_WAVE * 1024;
-  char* const b_dst = lds + A_BYTES + wave * B_PER_WAVE * 1024;
-  // L2 warm-up: two steps before a stage is copied, each lane touches one
-  // 16-byte piece of one A row and one B row of it (64 rows per wave), so the
-  // copy itself hits L2; the pieces land in a per-wave scratch kilobyte.
-  char* const junk = lds + kStages * STAGE + wave * 1024;
-  uint32_t pa_off, pb_off;
-  {
-    const int r = wave * 64 + lane;
-    const int rr = min(r, rows - 1);
-    if constexpr (GATEUP) {
-      pa_off = (uint32_t)a.row_token[row0 + rr] * (uint32_t)K;
-      pb_off = (uint32_t)((wave & 1) * 64 + lane) * (uint32_t)K;
-    } else {
-      pa_off = (uint32_t)rr * (uint32_t)K;
-      pb_off = (uint32_t)r * (uint32_t)K;
-    }
-  }
+  char* const b_dst = b_lds + wave * B_PER_WAVE * 1024;
 
   f32x16 acc[MB][4];
 #pragma unroll
@@ -228,76 +273,61 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   for (int kk = 0; kk < 4; ++kk) slot[kk] = ((kk * 2 + (lane >> 5)) ^ swz_of_row(lane & 15)) << 4;
 
   const int nk = K / kBK;
-  // prologue: steps 0 and 1 in flight (and step 3 warmed), wait for step 0
-  copy_rows<A_PER_WAVE>(abase, aoff, a_dst);
-  copy_rows<B_PER_WAVE>(bbase, boff, b_dst);
-  if (nk > 1) {
-    copy_rows<A_PER_WAVE>(abase + kBK, aoff, a_dst + STAGE);
-    copy_rows<B_PER_WAVE>(bbase + kBK, boff, b_dst + STAGE);
-  }
-  if (kPrefetchL2 && nk > 3) {
-    copy16(abase + 3 * kBK + pa_off, junk);
-    copy16(bbase + 3 * kBK + pb_off, junk);
-  }
-  if (nk > 3)
-    wait_vmem_upto<A_PER_WAVE + B_PER_WAVE + (kPrefetchL2 ? 2 : 0)>();
-  else if (nk > 1)
-    wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
-  else
-    wait_vmem_upto<0>();
+  constexpr int AH = A_PER_WAVE / 2, BH = B_PER_WAVE / 2;
+  // prologue: A of steps 0 and (half of) 1, B of steps 0 and 1 in flight
+  // (indices clamped to the last step: a re-copy lands in a stage that is not
+  // read again), then wait for step 0
+  const bf16* const a1 = abase + min(1, nk - 1) * kBK;
+  copy_rows<0, A_PER_WAVE>(abase, aoff, a_dst);
+  copy_rows<0, B_PER_WAVE>(bbase, boff, b_dst);
+  copy_rows<0, AH>(a1, aoff, a_dst + kAStage);
+  copy_rows<0, B_PER_WAVE>(bbase + min(1, nk - 1) * kBK, boff, b_dst + kBStage);
+  wait_vmem_upto<AH + B_PER_WAVE>();
   __builtin_amdgcn_s_barrier();
 
   bf16x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
-  load_frags<MB>(lds, arow, brow, slot[0], A_BYTES, fa0, fb0);
+  int sbi = 0;  // B stage of step kt (kt mod 3)
+  load_frags<MB>(lds, b_lds, arow, brow, slot[0], fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const char* sa = lds + cur * STAGE;
-    load_frags<MB>(sa, arow, brow, slot[1], A_BYTES, fa1, fb1);
+    const char* sa = lds + (kt & 1) * kAStage;
+    const char* sb = b_lds + sbi * kBStage;
+    const int sbn = sbi == kBStages - 1 ? 0 : sbi + 1;  // B stage of step kt+1
+    const int sbf = sbn == kBStages - 1 ? 0 : sbn + 1;  // B stage of step kt+2 (free)
+    const bf16* const an = abase + min(kt + 1, nk - 1) * kBK;
+    const bf16* const bn = bbase + min(kt + 2, nk - 1) * kBK;
+    // sub-step 0: second half of A of step kt+1
+    load_frags<MB>(sa, sb, arow, brow, slot[1], fa1, fb1);
+    copy_rows<AH, A_PER_WAVE - AH>(an, aoff, a_dst + ((kt + 1) & 1) * kAStage);
     mfma_step<MB>(fa0, fb0, acc);
-    interleave_reads<MB>();
-    load_frags<MB>(sa, arow, brow, slot[2], A_BYTES, fa0, fb0);
+    interleave_reads<MB, A_PER_WAVE - AH>();
+    // sub-steps 1 and 2: B of step kt+2
+    load_frags<MB>(sa, sb, arow, brow, slot[2], fa0, fb0);
+    copy_rows<0, BH>(bn, boff, b_dst + sbf * kBStage);
     mfma_step<MB>(fa1, fb1, acc);
-    interleave_reads<MB>();
-    load_frags<MB>(sa, arow, brow, slot[3], A_BYTES, fa1, fb1);
+    interleave_reads<MB, BH>();
+    load_frags<MB>(sa, sb, arow, brow, slot[3], fa1, fb1);
+    copy_rows<BH, B_PER_WAVE - BH>(bn, boff, b_dst + sbf * kBStage);
     mfma_step<MB>(fa0, fb0, acc);
-    interleave_reads<MB>();
-    // this wave's reads of the current stage are done and step kt+1 has
-    // landed (it is the only copy in flight); after the barrier every wave
-    // is past the current stage
+    interleave_reads<MB, B_PER_WAVE - BH>();
+    // this wave's reads of the current stages are done and A and B of step
+    // kt+1 have landed (copies complete in issue order; only B of step kt+2
+    // was issued after them); after the barrier every wave is past the
+    // current stages and sees step kt+1
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    // only the warm-up of step kt+3 was issued after step kt+1's copies
-    if (kPrefetchL2 && kt + 3 < nk)
-      wait_vmem_upto<2>();
-    else
-      wait_vmem_upto<0>();
+    wait_vmem_upto<B_PER_WAVE>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (kPrefetchL2 && kt + 4 < nk) {
-      const int k4 = (kt + 4) * kBK;
-      copy16(abase + k4 + pa_off, junk);
-      copy16(bbase + k4 + pb_off, junk);
-    }
-    // last sub-step: the freed stage is refilled with step kt+2 (the last two
-    // steps re-copy step nk-1, which keeps this region branch-free), step
-    // kt+1's first fragments are read (after the last step: a stage that is
-    // never used, harmless), and both interleave with the MFMAs
-    {
-      const int k2 = min(kt + 2, nk - 1) * kBK;
-      copy_rows<A_PER_WAVE>(abase + k2, aoff, a_dst + cur * STAGE);
-      copy_rows<B_PER_WAVE>(bbase + k2, boff, b_dst + cur * STAGE);
-    }
-    load_frags<MB>(lds + (cur ^ 1) * STAGE, arow, brow, slot[0], A_BYTES, fa0, fb0);
+    // last sub-step: first half of A of step kt+2 into the freed A stage and
+    // step kt+1's first fragments (after the last step: harmless reads of
+    // unused stages)
+    load_frags<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, slot[0], fa0, fb0);
+    copy_rows<0, AH>(abase + min(kt + 2, nk - 1) * kBK, aoff, a_dst + (kt & 1) * kAStage);
     mfma_step<MB>(fa1, fb1, acc);
-#pragma unroll
-    for (int i = 0; i < MB + 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global->LDS copy
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global->LDS copy
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, MB * 4 - (MB + 4), 0);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave_reads<MB, AH>();
+    sbi = sbn;
   }
+  // no copy may still be writing LDS when the stages are reused or released
+  wait_vmem_upto<0>();
 
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
@@ -326,21 +356,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes + (kPrefetchL2 ? 4096 : 0)];
-  int e, nt, row0, rows;
-  if (!tile_of_block(a, 2 * kWM, e, nt, row0, rows)) return;
-  if (rows > kWM)
-    gemm_tile<kWM, GATEUP>(a, lds, e, nt, row0, rows);
-  else
-    gemm_tile<kWM / 2, GATEUP>(a, lds, e, nt, row0, rows);
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  Work w;
+  if (!work_of_block(a, 2 * kWM, w)) return;
+  if (!w.pair) {
+    gemm_tile<kWM, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+  } else {
+    gemm_tile<kWM / 2, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+    if (w.nt + 1 < a.n_tiles) {
+      __syncthreads();  // every wave is past its last reads of the LDS stages
+      gemm_tile<kWM / 2, GATEUP>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+    }
+  }
 }
 
 // fp32 layers: one wavefront per 32 x 32 output tile on v_mfma_f32_32x32x2_f32,
 // operands straight from global memory (tiny layers only).
 template <bool GATEUP>
 __global__ __launch_bounds__(64) void expert_gemm_f32(GemmArgs a) {
-  int e, nt, row0, rows;
-  if (!tile_of_block(a, 32, e, nt, row0, rows)) return;
+  Work w;
+  if (!work_of_block(a, 32, w)) return;  // half_rows = 0: never a pair
+  const int e = w.e, nt = w.nt, row0 = w.row0, rows = w.rows;
   const int lane = threadIdx.x;
   const int K = a.K;
   const int rr = min(lane & 31, rows - 1);
@@ -371,15 +407,16 @@ __global__ __launch_bounds__(64) void expert_gemm_f32(GemmArgs a) {
   }
 }
 
-// Segments of every expert and the exclusive prefix of their row-tile counts.
+// Segments of every expert and the exclusive prefixes of its full and short
+// row-tile counts.
 __global__ __launch_bounds__(1024) void schedule_kernel(ScheduleArgs a) {
-  __shared__ int32_t buf[2][1024];
+  __shared__ int32_t bf[2][1024], bh[2][1024];
   const int tid = threadIdx.x;
   const int n_exp = a.E + a.S;
-  int carry = 0;
+  int carry_f = 0, carry_h = 0;
   for (int e0 = 0; e0 < n_exp; e0 += 1024) {
     const int e = e0 + tid;
-    int mt = 0;
+    int nf = 0, nh = 0;
     if (e < n_exp) {
       int start, len;
       if (e < a.E) {
@@ -391,22 +428,34 @@ __global__ __launch_bounds__(1024) void schedule_kernel(ScheduleArgs a) {
       }
       a.seg_start[e] = start;
       a.seg_len[e] = len;
-      mt = (len + a.BM - 1) / a.BM;
+      const int nrt = (len + a.BM - 1) / a.BM;
+      nh = (nrt > 0 && len - (nrt - 1) * a.BM <= a.half_rows) ? 1 : 0;
+      nf = nrt - nh;
     }
-    // inclusive Hillis-Steele scan over the 1024 entries
+    // inclusive Hillis-Steele scans over the 1024 entries
     int cur = 0;
-    buf[cur][tid] = mt;
+    bf[cur][tid] = nf;
+    bh[cur][tid] = nh;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-      const int v = buf[cur][tid] + (tid >= off ? buf[cur][tid - off] : 0);
-      buf[cur ^ 1][tid] = v;
+      const int vf = bf[cur][tid] + (tid >= off ? bf[cur][tid - off] : 0);
+      const int vh = bh[cur][tid] + (tid >= off ? bh[cur][tid - off] : 0);
+      bf[cur ^ 1][tid] = vf;
+      bh[cur ^ 1][tid] = vh;
       cur ^= 1;
       __syncthreads();
     }
-    const int incl = buf[cur][tid];
-    if (e < n_exp) a.mt_prefix[e] = carry + incl - mt;
-    if (e == n_exp - 1) a.mt_prefix[n_exp] = carry + incl;
-    carry += buf[cur][1023];
+    const int incl_f = bf[cur][tid], incl_h = bh[cur][tid];
+    if (e < n_exp) {
+      a.f_prefix[e] = carry_f + incl_f - nf;
+      a.h_prefix[e] = carry_h + incl_h - nh;
+    }
+    if (e == n_exp - 1) {
+      a.f_prefix[n_exp] = carry_f + incl_f;
+      a.h_prefix[n_exp] = carry_h + incl_h;
+    }
+    carry_f += bf[cur][1023];
+    carry_h += bh[cur][1023];
     __syncthreads();
   }
 }
@@ -415,8 +464,12 @@ __global__ __launch_bounds__(1024) void schedule_kernel(ScheduleArgs a) {
 
 int gemm_bm(int dtype) { return dtype == 1 ? 2 * kWM : 32; }
 
+int gemm_half_rows(int dtype) { return dtype == 1 ? kWM : 0; }
+
 int64_t gemm_mtile_bound(int T, int E, int S, int k, int BM) {
-  // sum_e ceil(n_e / BM) <= (sum_e n_e + E*(BM-1)) / BM, sum_e n_e <= T*k
+  // sum_e ceil(n_e / BM) <= (sum_e n_e + E*(BM-1)) / BM, sum_e n_e <= T*k;
+  // work items per GEMM <= row tiles * column tiles (a short-tile item covers
+  // two column tiles)
   return ((int64_t)T * k + (int64_t)E * (BM - 1)) / BM + (int64_t)S * ((T + BM - 1) / BM);
 }
 

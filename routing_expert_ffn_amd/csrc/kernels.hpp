@@ -48,13 +48,16 @@ struct PermuteArgs {
   int32_t* slot_row;        // [T,k]
 };
 
-// Row segments of the experts (routed then shared) and their m-tile prefix.
+// Row segments of the experts (routed then shared) and the prefixes of their
+// row-tile counts: full row tiles (more than half_rows rows) and short last
+// row tiles (at most half_rows rows; half_rows = 0 makes every tile full).
 struct ScheduleArgs {
-  int T, E, S, k, BM;
+  int T, E, S, k, BM, half_rows;
   const int32_t* offsets;   // [E+1]
   int32_t* seg_start;       // [E+S]
   int32_t* seg_len;         // [E+S]
-  int32_t* mt_prefix;       // [E+S+1]
+  int32_t* f_prefix;        // [E+S+1] full row tiles before expert e
+  int32_t* h_prefix;        // [E+S+1] short row tiles before expert e
 };
 
 struct GemmArgs {
@@ -68,7 +71,8 @@ struct GemmArgs {
   void* c;                  // gate/up: h [rows,I]; down: y_rows [rows,H]
   const int32_t* seg_start;
   const int32_t* seg_len;
-  const int32_t* mt_prefix;
+  const int32_t* f_prefix;
+  const int32_t* h_prefix;
 };
 
 struct CombineArgs {
@@ -106,6 +110,8 @@ hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
 // Upper bound of the m-tiles of all experts (grid sizing without a host sync).
 int64_t gemm_mtile_bound(int T, int E, int S, int k, int BM);
 int gemm_bm(int dtype);
+// Row count at or below which an expert's last row tile runs at half height.
+int gemm_half_rows(int dtype);
 hipError_t launch_gateup(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s);
