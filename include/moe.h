@@ -109,7 +109,10 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
  * 0x1.111112p-7, 0x1.6c16c2p-10, 0x1.a01a02p-13}.  Group score = fl32(best +
  * second best) of a group's c.  Ties rank the lower index first.
  * Capacity: tokens in index order each take their best-ranked allowed experts
- * with fewer than C tokens so far; C = ceil(((cf*T)*k)/E) in double. */
+ * with fewer than C tokens so far; C = ceil(((cf*T)*k)/E) in double.
+ * Workspace: required (MOE_ERR_WORKSPACE otherwise) with a capacity limit and
+ * for bf16 layers that compute their logits; fp32 layers and logits_in
+ * routing without a capacity limit may pass ws = NULL. */
 moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
                      const float* logit_bias, const float* sel_bias, const float* logits_in,
                      float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,

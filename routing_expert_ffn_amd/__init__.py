@@ -124,7 +124,7 @@ def route(cfg, T, x=None, w_router=None, logit_bias=None, sel_bias=None, logits_
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     if topk_w is None:
         topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    if ws is None and cfg.capacity_factor > 0:
+    if ws is None:
         ws = workspace(cfg, T, dev)
     _check(lib().moe_route(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(sel_bias), _p(logits_in),
                            _p(logits_out), _p(topk_idx), _p(topk_w), _p(expert_counts), _p(ws),

@@ -116,7 +116,7 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
 }
 
 struct Layout {
-  size_t logits, cand, idx, w, counts, offsets, slot_row, row_token, chunk_cnt, chunk_base, seg_start, seg_len,
+  size_t logits, rpart, cand, idx, w, counts, offsets, slot_row, row_token, chunk_cnt, chunk_base, seg_start, seg_len,
       f_prefix, h_prefix, h, y, total;
 };
 
@@ -132,6 +132,13 @@ Layout layout_of(const Dims& d) {
   const size_t rows = T * k + S * T;
   const size_t nchunks = (T + 63) / 64;
   L.logits = take(T * E * 4);
+  // partial router logits of the K slices (bf16 router GEMM, small T)
+  size_t nsplit = 1;
+  if (d.dtype == MOE_BF16 && d.T > 0) {
+    int sps;
+    nsplit = (size_t)router_splits(d.T, d.H, &sps);
+  }
+  L.rpart = take(nsplit > 1 ? nsplit * T * E * 4 : 0);
   L.cand = take(d.capacity > 0 ? T * (size_t)d.n_allowed * 4 : 0);
   L.idx = take(T * k * 4);
   L.w = take(T * k * 4);
@@ -186,6 +193,35 @@ RouteParams route_params(const Dims& d) {
 }
 
 // ---- stages (arguments already validated) -----------------------------------
+
+// Router: logits_in -> selection kernel; bf16 -> router GEMM (logits, or
+// partial logits of K slices) then the selection kernel, which adds the
+// slices and logit_bias and writes the logits to a.logits_out (or the
+// workspace); fp32 -> the fused fp32 router.
+hipError_t run_router(const Dims& d, RouterArgs a, const void* x, const void* w_router, void* ws, const Layout& L,
+                      hipStream_t s) {
+  if (a.logits_in) return timed(K_ROUTE_SELECT, s, [&] { return launch_route_select(a, s); });
+  if (d.dtype != MOE_BF16) return timed(K_ROUTER, s, [&] { return launch_router(a, d.dtype, s); });
+  int sps;
+  const int S = router_splits(d.T, d.H, &sps);
+  float* lg = a.logits_out ? a.logits_out : at<float>(ws, L.logits);
+  RouterGemmArgs g{};
+  g.T = (int)d.T;
+  g.H = d.H;
+  g.E = d.E;
+  g.S = S;
+  g.sps = sps;
+  g.x = x;
+  g.w = w_router;
+  g.out = S == 1 ? lg : at<float>(ws, L.rpart);
+  hipError_t e = timed(K_ROUTER, s, [&] { return launch_router_gemm(g, s); });
+  if (e != hipSuccess) return e;
+  a.part = g.out;
+  a.nsplit = S;
+  a.logits_out = lg;
+  return timed(K_ROUTE_SELECT, s, [&] { return launch_route_select(a, s); });
+}
+
 moe_status do_route(const Dims& d, const void* x, const void* w_router, const float* logit_bias,
                     const float* sel_bias, const float* logits_in, float* logits_out, int32_t* topk_idx,
                     float* topk_w, int32_t* counts, void* ws, const Layout& L, hipStream_t s) {
@@ -202,11 +238,12 @@ moe_status do_route(const Dims& d, const void* x, const void* w_router, const fl
   a.counts = nullptr;
   hipError_t e;
   if (d.capacity > 0) {
+    // the capacity pass reads the logits (gates of the final selection)
     float* lg = logits_out ? logits_out : at<float>(ws, L.logits);
     if (logits_in) lg = const_cast<float*>(logits_in);
     a.logits_out = logits_in ? nullptr : lg;
     a.cand = at<int32_t>(ws, L.cand);
-    e = timed(K_ROUTER, s, [&] { return launch_router(a, d.dtype, s); });
+    e = run_router(d, a, x, w_router, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "router kernel launch");
     if (logits_in && logits_out) {
       e = hipMemcpyAsync(logits_out, logits_in, sizeof(float) * d.T * d.E, hipMemcpyDeviceToDevice, s);
@@ -233,7 +270,7 @@ moe_status do_route(const Dims& d, const void* x, const void* w_router, const fl
     if (e != hipSuccess) return hip_fail(e, "logits copy");
     a.logits_out = nullptr;
   }
-  e = timed(K_ROUTER, s, [&] { return launch_router(a, d.dtype, s); });
+  e = run_router(d, a, x, w_router, ws, L, s);
   if (e != hipSuccess) return hip_fail(e, "router kernel launch");
   return MOE_OK;
 }
@@ -334,9 +371,9 @@ moe_status do_combine(const Dims& d, const void* y_rows, const int32_t* slot_row
 
 // ---- kernel names --------------------------------------------------------------
 const char* kernel_name(int id) {
-  static const char* names[K_COUNT] = {"fill",          "router",   "capacity", "permute_count",
-                                       "permute_scan",  "permute_scatter", "schedule", "gateup_swiglu",
-                                       "down",          "combine"};
+  static const char* names[K_COUNT] = {"fill",          "router",          "router_select", "capacity",
+                                       "permute_count", "permute_scan",    "permute_scatter", "schedule",
+                                       "gateup_swiglu", "down",            "combine"};
   return (id >= 0 && id < K_COUNT) ? names[id] : nullptr;
 }
 
@@ -364,7 +401,9 @@ moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void
     return fail(MOE_ERR_INVALID_ARG, "x and w_router must be 16-byte aligned");
   if (!topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "topk_idx and topk_w are required");
   Layout L{};
-  if (d.capacity > 0) {
+  // the workspace holds the capacity candidates, and for bf16 layers the
+  // router GEMM's logits and K-slice partials
+  if (d.capacity > 0 || (!logits_in && d.dtype == MOE_BF16)) {
     st = check_ws(d, ws, ws_bytes, L);
     if (st != MOE_OK) return st;
   }

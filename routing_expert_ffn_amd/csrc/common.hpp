@@ -81,3 +81,31 @@ __device__ __forceinline__ uint64_t rank_key(float score, int e) {
   return ((uint64_t)ordered_bits(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 __device__ __forceinline__ int key_expert(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu)); }
+
+// ---- global->LDS staging of 128-byte tile rows (grouped GEMMs, router GEMM)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wait until at most N of this wavefront's vector-memory operations (here the
+// global->LDS copies, which complete in order) are outstanding:
+// s_waitcnt vmcnt(N), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Tiles live in LDS as rows of 128 bytes (64 bf16 of K) whose eight 16-byte
+// chunks are permuted: chunk c of row r sits in slot c ^ sw(r) with
+// sw(r) = (r % 8) ^ ((r / 8) % 2).  Sixteen consecutive rows read at one chunk
+// then touch 16 distinct 16-byte bank groups, and so do any eight within a
+// 128-byte window: fragment reads are free of LDS bank conflicts.
+__device__ __forceinline__ int swz_of_row(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// One global->LDS copy of 16 bytes per lane: lane L reads src and writes LDS
+// bytes [dst + 16*L, dst + 16*L + 16) (dst is the same for the whole wave).
+// (A plain function: the builtin must not sit in a template or lambda, whose
+// host-side instantiation would drop the kernel's launch stub.)
+__device__ __forceinline__ void copy16(const bf16* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}

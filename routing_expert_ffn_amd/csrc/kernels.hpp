@@ -16,8 +16,10 @@ struct RouteParams {
 
 struct RouterArgs {
   RouteParams p;
-  const void* x;            // [T,H] (ignored when logits_in)
-  const void* w_router;     // [E,H]
+  const void* x;            // [T,H] (fused fp32 router only)
+  const void* w_router;     // [E,H] (fused fp32 router only)
+  const float* part;        // selection kernel: [nsplit,T,E] partial logits without bias
+  int nsplit;               //   (summed in order, then logit_bias added)
   const float* logit_bias;  // [E] or null
   const float* sel_bias;    // [E] or null
   const float* logits_in;   // [T,E] or null: route these logits
@@ -26,6 +28,15 @@ struct RouterArgs {
   float* topk_w;            // [T,k]
   int32_t* counts;          // [E] atomically incremented, or null
   int32_t* cand;            // capacity mode: [T,n_allowed] experts in rank order
+};
+
+// Router GEMM (bf16): logits of 64-token tiles over K slices of sps steps of
+// 64; out is [T,E] when S == 1, else [S,T,E] partial sums.
+struct RouterGemmArgs {
+  int T, H, E, S, sps;
+  const void* x;            // [T,H]
+  const void* w;            // [E,H]
+  float* out;
 };
 
 struct CapacityArgs {
@@ -87,6 +98,7 @@ struct CombineArgs {
 enum KernelId {
   K_FILL = 0,
   K_ROUTER,
+  K_ROUTE_SELECT,
   K_CAPACITY,
   K_PERM_COUNT,
   K_PERM_SCAN,
@@ -101,7 +113,13 @@ enum KernelId {
 const char* kernel_name(int id);
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+// Fused fp32 router (GEMM on fp32 MFMA + selection).
 hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s);
+// K slices of the bf16 router GEMM for T tokens (>= 1) and its launch.
+int router_splits(int64_t T, int H, int* sps);
+hipError_t launch_router_gemm(const RouterGemmArgs& a, hipStream_t s);
+// Selection from partial logits (a.part, a.nsplit) or from a.logits_in.
+hipError_t launch_route_select(const RouterArgs& a, hipStream_t s);
 hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s);
 hipError_t launch_perm_count(const PermuteArgs& a, hipStream_t s);
 hipError_t launch_perm_scan(const PermuteArgs& a, hipStream_t s);

@@ -15,6 +15,8 @@
 //
 // This translation unit is compiled without floating-point contraction so the
 // fp32 sigmoid below is exactly the documented sequence of roundings.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -213,6 +215,163 @@ __device__ __forceinline__ void wave_bitonic_desc(uint64_t (&key)[NJ], int lane)
   }
 }
 
+// Route token t from its logits row (lane holds experts j*64 + lane): group
+// limit and top-k with gates, or in capacity mode the ranked candidates.
+template <int NJ>
+__device__ __forceinline__ void route_token(const RouterArgs& a, const float* lrow, int t, int lane) {
+  const RouteParams& p = a.p;
+  uint64_t key[NJ];
+  token_scores<NJ>(p, lrow, a.sel_bias, lane, key);
+  if (p.capacity > 0) {
+    wave_bitonic_desc<NJ>(key, lane);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int i = j * MOE_WAVE + lane;
+      if (i < p.n_allowed) a.cand[(int64_t)t * p.n_allowed + i] = key_expert(key[j]);
+    }
+  } else {
+    const int my_e = token_topk<NJ>(p, key, lane);
+    const float g = token_gate<NJ>(p, lrow, my_e, lane);
+    if (lane < p.k) {
+      a.topk_idx[(int64_t)t * p.k + lane] = my_e;
+      a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
+      if (a.counts && my_e >= 0) atomicAdd(&a.counts[my_e], 1);
+    }
+  }
+}
+
+// ---- bf16 router: GEMM kernel, then one wavefront per token -----------------
+
+// Router GEMM tile: 64 tokens x 128*NB experts (wave w: experts w*32*NB ..,
+// all 64 tokens, 2 x NB MFMA blocks of 32x32) over one K slice.  x rows and
+// weight rows are staged in LDS in the swizzled 128-byte row format, two
+// stages, the next step copied while the current one computes.
+template <int NB>
+__global__ __launch_bounds__(256) void router_gemm_kernel(RouterGemmArgs a) {
+  constexpr int EP = 128 * NB;
+  constexpr int A_BYTES = 64 * 128;
+  constexpr int STAGE = A_BYTES + EP * 128;
+  constexpr int B_PER_WAVE = EP / 8 / 4;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 64;
+  const int nk = a.H / 64;
+  const int kb = blockIdx.y * a.sps, ke = min(nk, kb + a.sps);
+  const int lrow = lane >> 3;
+  const bf16* x = static_cast<const bf16*>(a.x);
+  const bf16* w = static_cast<const bf16*>(a.w);
+  uint32_t aoff[2], boff[B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave * 2 + i) * 8 + lrow;
+    const int tok = min(t0 + r, a.T - 1);
+    aoff[i] = (uint32_t)tok * (uint32_t)a.H + ((lane & 7) ^ swz_of_row(r)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_PER_WAVE; ++i) {
+    const int r = (wave * B_PER_WAVE + i) * 8 + lrow;
+    const int e = min(r, a.E - 1);
+    boff[i] = (uint32_t)e * (uint32_t)a.H + ((lane & 7) ^ swz_of_row(r)) * 8;
+  }
+  char* const a_dst = lds + wave * 2 * 1024;
+  char* const b_dst = lds + A_BYTES + wave * B_PER_WAVE * 1024;
+  f32x16 acc[2][NB];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+  // fragment rows are congruent to lane mod 16: the swizzled slot depends on
+  // the lane and the 16-wide sub-step only
+  int slot[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) slot[kk] = ((kk * 2 + (lane >> 5)) ^ swz_of_row(lane & 15)) << 4;
+  const int arow = (lane & 31) * 128;
+  const int brow = A_BYTES + (wave * 32 * NB + (lane & 31)) * 128;
+
+  if (kb < ke) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy16(x + kb * 64 + aoff[i], a_dst + i * 1024);
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) copy16(w + kb * 64 + boff[i], b_dst + i * 1024);
+  }
+  for (int ks = kb; ks < ke; ++ks) {
+    const int cur = (ks - kb) & 1;
+    // step ks has landed for every wave, and every wave is done with the
+    // other stage (read in the previous step)
+    wait_vmem_upto<0>();
+    __syncthreads();
+    if (ks + 1 < ke) {
+      const int k1 = (ks + 1) * 64;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) copy16(x + k1 + aoff[i], a_dst + (cur ^ 1) * STAGE + i * 1024);
+#pragma unroll
+      for (int i = 0; i < B_PER_WAVE; ++i) copy16(w + k1 + boff[i], b_dst + (cur ^ 1) * STAGE + i * 1024);
+    }
+    const char* st = lds + cur * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 fa[2], fb[NB];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) fa[m] = *reinterpret_cast<const bf16x8*>(st + arow + m * 32 * 128 + slot[kk]);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) fb[n] = *reinterpret_cast<const bf16x8*>(st + brow + n * 32 * 128 + slot[kk]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+    }
+  }
+  float* out = a.out + (int64_t)blockIdx.y * a.T * a.E;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int e = wave * 32 * NB + n * 32 + (lane & 31);
+    if (e >= a.E) continue;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = t0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (tok < a.T) out[(int64_t)tok * a.E + e] = acc[m][n][r];
+      }
+  }
+}
+
+// Selection: one wavefront per token.  The token's logits are the sum of its
+// nsplit partial rows (in slice order) plus logit_bias, or logits_in as
+// given; they are written to logits_out when set, kept in LDS, and routed.
+template <int NJ>
+__global__ __launch_bounds__(256) void route_select_kernel(RouterArgs a) {
+  __shared__ float lds_rows[4][NJ * MOE_WAVE];
+  const RouteParams& p = a.p;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= p.T) return;
+  float* lrow = lds_rows[wave];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = j * MOE_WAVE + lane;
+    if (e >= p.E) continue;
+    float v;
+    if (a.logits_in) {
+      v = a.logits_in[(int64_t)t * p.E + e];
+    } else {
+      v = 0.0f;
+      for (int sl = 0; sl < a.nsplit; ++sl) v += a.part[((int64_t)sl * p.T + t) * p.E + e];
+      if (a.logit_bias) v += a.logit_bias[e];
+    }
+    lrow[e] = v;
+    if (a.logits_out) a.logits_out[(int64_t)t * p.E + e] = v;
+  }
+  // the row is read across lanes below: the wave's LDS writes complete first
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  route_token<NJ>(a, lrow, t, lane);
+}
+
+// ---- fp32 layers: fused router ------------------------------------------------
+
 constexpr int kRouterTokens = 32;
 
 // One workgroup: 32 tokens x all experts.  The GEMM runs on 32x32 MFMA tiles
@@ -302,25 +461,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   for (int r = wave; r < kRouterTokens; r += 4) {
     const int t = t0 + r;
     if (t >= p.T) break;
-    const float* lrow = lds_logits + r * EP;
-    uint64_t key[NJ];
-    token_scores<NJ>(p, lrow, a.sel_bias, lane, key);
-    if (p.capacity > 0) {
-      wave_bitonic_desc<NJ>(key, lane);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int i = j * MOE_WAVE + lane;
-        if (i < p.n_allowed) a.cand[(int64_t)t * p.n_allowed + i] = key_expert(key[j]);
-      }
-    } else {
-      const int my_e = token_topk<NJ>(p, key, lane);
-      const float g = token_gate<NJ>(p, lrow, my_e, lane);
-      if (lane < p.k) {
-        a.topk_idx[(int64_t)t * p.k + lane] = my_e;
-        a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
-        if (a.counts && my_e >= 0) atomicAdd(&a.counts[my_e], 1);
-      }
-    }
+    route_token<NJ>(a, lds_logits + r * EP, t, lane);
   }
 }
 
@@ -388,6 +529,20 @@ hipError_t launch_router_d(const RouterArgs& a, hipStream_t s) {
   return launch_router_t<Tin, 8>(a, s);
 }
 
+template <int NB>
+hipError_t launch_router_gemm_t(const RouterGemmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)a.S);
+  hipLaunchKernelGGL((router_gemm_kernel<NB>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int NJ>
+hipError_t launch_route_select_t(const RouterArgs& a, hipStream_t s) {
+  const int grid = (a.p.T + 3) / 4;
+  hipLaunchKernelGGL((route_select_kernel<NJ>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int NJ>
 hipError_t launch_capacity_t(const CapacityArgs& a, hipStream_t s) {
   const size_t lds = sizeof(int32_t) * (a.p.E + MOE_MAX_TOPK);
@@ -400,6 +555,35 @@ hipError_t launch_capacity_t(const CapacityArgs& a, hipStream_t s) {
 hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s) {
   if (a.p.T <= 0) return hipSuccess;
   return dtype == 1 ? launch_router_d<bf16>(a, s) : launch_router_d<float>(a, s);
+}
+
+int router_splits(int64_t T, int H, int* sps) {
+  // enough (token tile, K slice) workgroups to cover the chip: 64-token
+  // tiles, K split into slices of whole 64-wide steps, at most 32 slices
+  const int nk = H / 64;
+  const int64_t tiles = (T + 63) / 64;
+  int S = 1;
+  if (tiles < 256) S = (int)std::min<int64_t>((256 + tiles - 1) / tiles, 32);
+  S = std::min(S, nk);
+  const int per = (nk + S - 1) / S;
+  *sps = per;
+  return (nk + per - 1) / per;
+}
+
+hipError_t launch_router_gemm(const RouterGemmArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.E <= 128) return launch_router_gemm_t<1>(a, s);
+  if (a.E <= 256) return launch_router_gemm_t<2>(a, s);
+  return launch_router_gemm_t<4>(a, s);
+}
+
+hipError_t launch_route_select(const RouterArgs& a, hipStream_t s) {
+  if (a.p.T <= 0) return hipSuccess;
+  const int nj = (a.p.E + MOE_WAVE - 1) / MOE_WAVE;
+  if (nj <= 1) return launch_route_select_t<1>(a, s);
+  if (nj <= 2) return launch_route_select_t<2>(a, s);
+  if (nj <= 4) return launch_route_select_t<4>(a, s);
+  return launch_route_select_t<8>(a, s);
 }
 
 hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s) {

@@ -101,6 +101,19 @@ def test_null_and_short_workspace_rejected_before_launch():
     assert L.moe_combine(ctypes.byref(c), -1, fake, fake, fake, fake, None) == -1
 
 
+def test_route_needs_workspace_when_it_computes_bf16_logits():
+    """bf16 routing from x writes logits (and K-slice partials) into the
+    workspace: a NULL or short workspace is an error before any launch, while
+    routing given logits without a capacity limit needs none."""
+    L = moe.lib()
+    c = moe.make_config(TEST_SHAPES["v3_small"])  # bf16, no capacity limit
+    fake = ctypes.c_void_p(256 * 1024)
+    st = L.moe_route(ctypes.byref(c), 16, fake, fake, None, None, None, None, fake, fake, None, None, 0, None)
+    assert st == -3 and "workspace" in L.moe_last_error().decode()
+    st = L.moe_route(ctypes.byref(c), 16, fake, fake, None, None, None, None, fake, fake, None, fake, 256, None)
+    assert st == -3
+
+
 def test_empty_batch_is_a_noop():
     L = moe.lib()
     c = moe.make_config(TEST_SHAPES["v3_small"])
