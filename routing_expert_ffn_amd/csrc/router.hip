@@ -465,46 +465,65 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   }
 }
 
-// Capacity pass: one wavefront serves the tokens in index order; lane r of a
-// step looks at rank base+r of the token's allowed experts, those with room
-// are taken in rank order until k are chosen.
+// Capacity pass, one workgroup of kCapWaves wavefronts, tokens in chunks of
+// `chunk`: every thread copies the chunk's ranked candidates to LDS; wave 0
+// then serves the chunk's tokens in index order (lane r of a step looks at
+// rank base+r; candidates with room are taken in rank order until k are
+// chosen; counts live in LDS); finally all waves compute the gates of the
+// chunk's tokens in parallel.
+constexpr int kCapWaves = 8;
+
 template <int NJ>
-__global__ __launch_bounds__(64) void capacity_kernel(CapacityArgs a) {
-  extern __shared__ int32_t lds_cnt[];  // [E] then 32 slots
-  int32_t* sel = lds_cnt + a.p.E;
+__global__ __launch_bounds__(kCapWaves * 64) void capacity_kernel(CapacityArgs a, int chunk) {
+  extern __shared__ int32_t lds_cap[];
   const RouteParams& p = a.p;
-  const int lane = threadIdx.x;
-  for (int e = lane; e < p.E; e += MOE_WAVE) lds_cnt[e] = 0;
-  __syncthreads();
   const int NA = p.n_allowed;
-  for (int t = 0; t < p.T; ++t) {
-    int got = 0;
-    for (int base = 0; base < NA && got < p.k; base += MOE_WAVE) {
-      const int r = base + lane;
-      const int e = r < NA ? a.cand[(int64_t)t * NA + r] : -1;
-      const bool room = e >= 0 && lds_cnt[e] < p.capacity;
-      const uint64_t m = __ballot(room);
-      const int need = p.k - got;
-      const int pre = __popcll(m & ((1ull << lane) - 1ull));
-      if (room && pre < need) {
-        lds_cnt[e] += 1;
-        sel[got + pre] = e;
+  int32_t* cnt = lds_cap;                   // [E]
+  int32_t* cand = cnt + p.E;                // [chunk][NA]
+  int32_t* sel = cand + chunk * NA;         // [chunk][k]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < p.E; e += kCapWaves * 64) cnt[e] = 0;
+  for (int t0 = 0; t0 < p.T; t0 += chunk) {
+    const int nt = min(chunk, p.T - t0);
+    __syncthreads();  // previous chunk's gates are done with sel
+    for (int i = tid; i < nt * NA; i += kCapWaves * 64) cand[i] = a.cand[(int64_t)t0 * NA + i];
+    __syncthreads();
+    if (wave == 0) {
+      for (int tt = 0; tt < nt; ++tt) {
+        const int32_t* c = cand + tt * NA;
+        int32_t* s = sel + tt * p.k;
+        int got = 0;
+        for (int base = 0; base < NA && got < p.k; base += MOE_WAVE) {
+          const int r = base + lane;
+          const int e = r < NA ? c[r] : -1;
+          const bool room = e >= 0 && cnt[e] < p.capacity;
+          const uint64_t m = __ballot(room);
+          const int need = p.k - got;
+          const int pre = __popcll(m & ((1ull << lane) - 1ull));
+          if (room && pre < need) {
+            cnt[e] += 1;
+            s[got + pre] = e;
+          }
+          const int avail = __popcll(m);
+          got += avail < need ? avail : need;
+        }
+        if (lane >= got && lane < p.k) s[lane] = -1;
       }
-      const int avail = __popcll(m);
-      got += avail < need ? avail : need;
-      __syncthreads();
-    }
-    const int my_e = lane < got ? sel[lane] : -1;
-    const float* lrow = a.logits + (int64_t)t * p.E;
-    const float g = token_gate<NJ>(p, lrow, my_e, lane);
-    if (lane < p.k) {
-      a.topk_idx[(int64_t)t * p.k + lane] = my_e;
-      a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
     }
     __syncthreads();
+    for (int tt = wave; tt < nt; tt += kCapWaves) {
+      const int t = t0 + tt;
+      const int my_e = lane < p.k ? sel[tt * p.k + lane] : -1;
+      const float g = token_gate<NJ>(p, a.logits + (int64_t)t * p.E, my_e, lane);
+      if (lane < p.k) {
+        a.topk_idx[(int64_t)t * p.k + lane] = my_e;
+        a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
+      }
+    }
   }
+  __syncthreads();
   if (a.counts)
-    for (int e = lane; e < p.E; e += MOE_WAVE) a.counts[e] = lds_cnt[e];
+    for (int e = tid; e < p.E; e += kCapWaves * 64) a.counts[e] = cnt[e];
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -545,8 +564,12 @@ hipError_t launch_route_select_t(const RouterArgs& a, hipStream_t s) {
 
 template <int NJ>
 hipError_t launch_capacity_t(const CapacityArgs& a, hipStream_t s) {
-  const size_t lds = sizeof(int32_t) * (a.p.E + MOE_MAX_TOPK);
-  hipLaunchKernelGGL((capacity_kernel<NJ>), dim3(1), dim3(64), lds, s, a);
+  // chunk: candidates and selections of as many tokens as fit, with the
+  // counts, in 64 KB of LDS (E <= 512, n_allowed <= E, k <= 32)
+  const int NA = a.p.n_allowed;
+  const int chunk = std::max(1, std::min(a.p.T, 15360 / (NA + a.p.k)));
+  const size_t lds = sizeof(int32_t) * ((size_t)a.p.E + (size_t)chunk * NA + (size_t)chunk * a.p.k);
+  hipLaunchKernelGGL((capacity_kernel<NJ>), dim3(1), dim3(kCapWaves * 64), lds, s, a, chunk);
   return hipGetLastError();
 }
 
