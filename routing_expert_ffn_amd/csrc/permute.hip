@@ -8,10 +8,12 @@
 //   count   one wavefront per 64-token chunk: LDS bit masks mask[e] (bit =
 //           token of the chunk routed to e, set with LDS atomics), chunk
 //           count = popcount;
-//   scan    per expert, exclusive prefix over chunks (chunk base) and the
-//           total; exclusive prefix over experts (offsets);
-//   scatter row = offsets[e] + base[chunk][e] + popcount(mask[e] below the
-//           token's bit), no float atomics and no order dependence.
+//   scan    one workgroup per expert: exclusive prefix over chunks (chunk
+//           base) and the total (count);
+//   scatter each chunk's workgroup scans the counts over experts (offsets;
+//           chunk 0 stores them), row = offsets[e] + base[chunk][e] +
+//           popcount(mask[e] below the token's bit); no float atomics and
+//           no order dependence.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,63 +43,82 @@ __global__ __launch_bounds__(64) void perm_count_kernel(PermuteArgs a) {
     a.chunk_cnt[(int64_t)chunk * a.E + e] = __popcll(lds_mask[e]);
 }
 
-// One workgroup of 1024 threads: `tpe` threads per expert split the chunks,
-// then the experts are scanned.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(PermuteArgs a) {
-  extern __shared__ int32_t lds_scan[];  // [1024] partial sums, then [E] totals
-  const int tid = threadIdx.x;
-  const int tpe = max(1, 1024 / a.E);                // threads per expert
-  const int per = (a.nchunks + tpe - 1) / tpe;       // chunks per thread
-  int32_t* part = lds_scan;
-  int32_t* tot = lds_scan + 1024;
-  for (int e0 = 0; e0 < a.E; e0 += 1024 / tpe) {
-    const int e = e0 + tid / tpe;
-    const int q = tid % tpe;
-    const bool act = e < a.E && tid / tpe < 1024 / tpe;
-    int sum = 0;
-    if (act) {
-      const int c1 = min(a.nchunks, (q + 1) * per);
-      for (int c = q * per; c < c1; ++c) sum += a.chunk_cnt[(int64_t)c * a.E + e];
-    }
-    part[tid] = sum;
-    __syncthreads();
-    int before = 0;
-    if (act) {
-      for (int r = 0; r < q; ++r) before += part[tid - q + r];
-      int run = before;
-      const int c1 = min(a.nchunks, (q + 1) * per);
-      for (int c = q * per; c < c1; ++c) {
-        const int v = a.chunk_cnt[(int64_t)c * a.E + e];
-        a.chunk_base[(int64_t)c * a.E + e] = run;
-        run += v;
-      }
-      if (q == tpe - 1) tot[e] = run;
-    }
-    __syncthreads();
+// Exclusive prefix sum over the 256 threads of a workgroup (sh: 4 ints of
+// LDS); *total receives the sum of all values.
+__device__ __forceinline__ int block_exclusive_scan_256(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < MOE_WAVE; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
-  // exclusive scan of the totals over experts (single thread per 1024 is
-  // enough: E <= 1024 and this runs once per layer call)
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < a.E; ++e) {
-      a.counts[e] = tot[e];
-      a.offsets[e] = run;
-      run += tot[e];
-    }
-    a.offsets[a.E] = run;
-    tot[0] = run;  // reuse: number of assigned rows
-  }
+  if (lane == MOE_WAVE - 1) sh[wave] = incl;
   __syncthreads();
-  const int assigned = tot[0];
-  const int64_t routed_rows = (int64_t)a.T * a.k;
-  for (int64_t r = assigned + tid; r < routed_rows; r += 1024) a.row_token[r] = -1;
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += sh[w];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  return before + incl - v;
+}
+
+// One workgroup per expert: thread i owns a contiguous range of chunks.
+__global__ __launch_bounds__(256) void perm_scan_kernel(PermuteArgs a) {
+  __shared__ int sh[4];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int per = (a.nchunks + 255) / 256;
+  const int c0 = min(a.nchunks, tid * per), c1 = min(a.nchunks, c0 + per);
+  int sum = 0;
+  int c = c0;
+  for (; c + 8 <= c1; c += 8) {
+    int q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = a.chunk_cnt[(int64_t)(c + i) * a.E + e];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += q[i];
+  }
+  for (; c < c1; ++c) sum += a.chunk_cnt[(int64_t)c * a.E + e];
+  int total;
+  int run = block_exclusive_scan_256(sum, sh, &total);
+  for (c = c0; c < c1; ++c) {
+    const int v = a.chunk_cnt[(int64_t)c * a.E + e];
+    a.chunk_base[(int64_t)c * a.E + e] = run;
+    run += v;
+  }
+  if (tid == 0) a.counts[e] = total;
 }
 
 __global__ __launch_bounds__(64) void perm_scatter_kernel(PermuteArgs a) {
-  extern __shared__ uint64_t lds_mask[];
+  extern __shared__ uint64_t lds_mask[];  // [E] masks, then [E+1] offsets
+  int32_t* off = reinterpret_cast<int32_t*>(lds_mask + a.E);
   const int chunk = blockIdx.x;
-  build_masks(a, chunk, lds_mask);
   const int lane = threadIdx.x;
+  // offsets: exclusive prefix of the counts over experts, lane l summing the
+  // experts [l*per, (l+1)*per) (E <= 512)
+  {
+    const int per = (a.E + MOE_WAVE - 1) / MOE_WAVE;
+    const int e0 = min(a.E, lane * per), e1 = min(a.E, e0 + per);
+    int sum = 0;
+    for (int e = e0; e < e1; ++e) sum += a.counts[e];
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - sum;
+    for (int e = e0; e < e1; ++e) {
+      off[e] = run;
+      run += a.counts[e];
+    }
+    if (lane == MOE_WAVE - 1) off[a.E] = incl;
+  }
+  build_masks(a, chunk, lds_mask);  // its barriers also publish off[]
+  if (chunk == 0)
+    for (int e = lane; e <= a.E; e += MOE_WAVE) a.offsets[e] = off[e];
+  // routed rows past the assigned ones (dropped slots) hold no token
+  const int64_t routed_rows = (int64_t)a.T * a.k;
+  for (int64_t r = off[a.E] + (int64_t)chunk * kChunk + lane; r < routed_rows; r += (int64_t)a.nchunks * kChunk)
+    a.row_token[r] = -1;
   const int t = chunk * kChunk + lane;
   if (t >= a.T) return;
   const uint64_t below = (1ull << lane) - 1ull;
@@ -105,7 +126,7 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(PermuteArgs a) {
     const int e = a.topk_idx[(int64_t)t * a.k + j];
     int row = -1;
     if (e >= 0 && e < a.E) {
-      row = a.offsets[e] + a.chunk_base[(int64_t)chunk * a.E + e] + __popcll(lds_mask[e] & below);
+      row = off[e] + a.chunk_base[(int64_t)chunk * a.E + e] + __popcll(lds_mask[e] & below);
       a.row_token[row] = t;
     }
     a.slot_row[(int64_t)t * a.k + j] = row;
@@ -124,12 +145,13 @@ hipError_t launch_perm_count(const PermuteArgs& a, hipStream_t s) {
 
 hipError_t launch_perm_scan(const PermuteArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), sizeof(int32_t) * (1024 + a.E), s, a);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(a.E), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_perm_scatter(const PermuteArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(a.nchunks), dim3(64), sizeof(uint64_t) * a.E, s, a);
+  const size_t lds = sizeof(uint64_t) * a.E + sizeof(int32_t) * (a.E + 1);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(a.nchunks), dim3(64), lds, s, a);
   return hipGetLastError();
 }

@@ -357,8 +357,19 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouterArgs a) {
     if (a.logits_in) {
       v = a.logits_in[(int64_t)t * p.E + e];
     } else {
+      // slices added in order; loads issued eight at a time
+      const float* src = a.part + (int64_t)t * p.E + e;
+      const int64_t stride = (int64_t)p.T * p.E;
       v = 0.0f;
-      for (int sl = 0; sl < a.nsplit; ++sl) v += a.part[((int64_t)sl * p.T + t) * p.E + e];
+      int sl = 0;
+      for (; sl + 8 <= a.nsplit; sl += 8) {
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = src[(sl + i) * stride];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v += q[i];
+      }
+      for (; sl < a.nsplit; ++sl) v += src[sl * stride];
       if (a.logit_bias) v += a.logit_bias[e];
     }
     lrow[e] = v;
