@@ -349,31 +349,46 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouterArgs a) {
   const int t = blockIdx.x * 4 + wave;
   if (t >= p.T) return;
   float* lrow = lds_rows[wave];
+  const int64_t stride = (int64_t)p.T * p.E;
+  if (!a.logits_in && a.nsplit > 1 && (p.E & 3) == 0 && (reinterpret_cast<uintptr_t>(a.part) & 15) == 0) {
+    // several K slices: lane l adds the slices of experts 4*(l + 64*q) .. +3
+    // with 16-byte loads, slices in order, eight loads in flight
+    for (int e0 = 4 * lane; e0 < p.E; e0 += 4 * MOE_WAVE) {
+      const float* src = a.part + (int64_t)t * p.E + e0;
+      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int sl = 0; sl < a.nsplit; sl += 8) {
+        f32x4 q[8];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int e = j * MOE_WAVE + lane;
-    if (e >= p.E) continue;
-    float v;
-    if (a.logits_in) {
-      v = a.logits_in[(int64_t)t * p.E + e];
-    } else {
-      // slices added in order; loads issued eight at a time
-      const float* src = a.part + (int64_t)t * p.E + e;
-      const int64_t stride = (int64_t)p.T * p.E;
-      v = 0.0f;
-      int sl = 0;
-      for (; sl + 8 <= a.nsplit; sl += 8) {
-        float q[8];
+        for (int i = 0; i < 8; ++i)
+          if (sl + i < a.nsplit) q[i] = *reinterpret_cast<const f32x4*>(src + (sl + i) * stride);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = src[(sl + i) * stride];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v += q[i];
+        for (int i = 0; i < 8; ++i)
+          if (sl + i < a.nsplit) v += q[i];
       }
-      for (; sl < a.nsplit; ++sl) v += src[sl * stride];
-      if (a.logit_bias) v += a.logit_bias[e];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float x = v[c];
+        if (a.logit_bias) x += a.logit_bias[e0 + c];
+        lrow[e0 + c] = x;
+        if (a.logits_out) a.logits_out[(int64_t)t * p.E + e0 + c] = x;
+      }
     }
-    lrow[e] = v;
-    if (a.logits_out) a.logits_out[(int64_t)t * p.E + e] = v;
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * MOE_WAVE + lane;
+      if (e >= p.E) continue;
+      float v;
+      if (a.logits_in) {
+        v = a.logits_in[(int64_t)t * p.E + e];
+      } else {
+        v = 0.0f;
+        for (int sl = 0; sl < a.nsplit; ++sl) v += a.part[(int64_t)t * p.E + e + sl * stride];
+        if (a.logit_bias) v += a.logit_bias[e];
+      }
+      lrow[e] = v;
+      if (a.logits_out) a.logits_out[(int64_t)t * p.E + e] = v;
+    }
   }
   // the row is read across lanes below: the wave's LDS writes complete first
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -480,8 +495,8 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 // `chunk`: every thread copies the chunk's ranked candidates to LDS; wave 0
 // then serves the chunk's tokens in index order (lane r of a step looks at
 // rank base+r; candidates with room are taken in rank order until k are
-// chosen; counts live in LDS); finally all waves compute the gates of the
-// chunk's tokens in parallel.
+// chosen; counts live in LDS); all threads store the chunk's selections.
+// The gates follow in capacity_gates_kernel, one wavefront per token.
 constexpr int kCapWaves = 8;
 
 template <int NJ>
@@ -500,41 +515,56 @@ __global__ __launch_bounds__(kCapWaves * 64) void capacity_kernel(CapacityArgs a
     for (int i = tid; i < nt * NA; i += kCapWaves * 64) cand[i] = a.cand[(int64_t)t0 * NA + i];
     __syncthreads();
     if (wave == 0) {
-      for (int tt = 0; tt < nt; ++tt) {
-        const int32_t* c = cand + tt * NA;
-        int32_t* s = sel + tt * p.k;
-        int got = 0;
-        for (int base = 0; base < NA && got < p.k; base += MOE_WAVE) {
-          const int r = base + lane;
-          const int e = r < NA ? c[r] : -1;
-          const bool room = e >= 0 && cnt[e] < p.capacity;
-          const uint64_t m = __ballot(room);
-          const int need = p.k - got;
-          const int pre = __popcll(m & ((1ull << lane) - 1ull));
-          if (room && pre < need) {
-            cnt[e] += 1;
-            s[got + pre] = e;
+      // the first 64 ranked candidates of 8 tokens are read ahead into
+      // registers; the serial chain per token is then one LDS gather of the
+      // counts, a ballot and the count updates
+      for (int tb = 0; tb < nt; tb += 8) {
+        int c0[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c0[i] = lane < NA ? cand[min(tb + i, nt - 1) * NA + lane] : -1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tt = tb + i;
+          if (tt >= nt) break;
+          const int32_t* c = cand + tt * NA;
+          int32_t* s = sel + tt * p.k;
+          int got = 0;
+          for (int base = 0; base < NA && got < p.k; base += MOE_WAVE) {
+            const int r = base + lane;
+            const int e = base == 0 ? c0[i] : (r < NA ? c[r] : -1);
+            const bool room = e >= 0 && cnt[e] < p.capacity;
+            const uint64_t m = __ballot(room);
+            const int need = p.k - got;
+            const int pre = __popcll(m & ((1ull << lane) - 1ull));
+            if (room && pre < need) {
+              atomicAdd(&cnt[e], 1);
+              s[got + pre] = e;
+            }
+            const int avail = __popcll(m);
+            got += avail < need ? avail : need;
           }
-          const int avail = __popcll(m);
-          got += avail < need ? avail : need;
+          if (lane >= got && lane < p.k) s[lane] = -1;
         }
-        if (lane >= got && lane < p.k) s[lane] = -1;
       }
     }
     __syncthreads();
-    for (int tt = wave; tt < nt; tt += kCapWaves) {
-      const int t = t0 + tt;
-      const int my_e = lane < p.k ? sel[tt * p.k + lane] : -1;
-      const float g = token_gate<NJ>(p, a.logits + (int64_t)t * p.E, my_e, lane);
-      if (lane < p.k) {
-        a.topk_idx[(int64_t)t * p.k + lane] = my_e;
-        a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
-      }
-    }
+    for (int i = tid; i < nt * p.k; i += kCapWaves * 64) a.topk_idx[(int64_t)t0 * p.k + i] = sel[i];
   }
   __syncthreads();
   if (a.counts)
     for (int e = tid; e < p.E; e += kCapWaves * 64) a.counts[e] = cnt[e];
+}
+
+// Gates of the final (capacity-limited) selection, one wavefront per token.
+template <int NJ>
+__global__ __launch_bounds__(256) void capacity_gates_kernel(CapacityArgs a) {
+  const RouteParams& p = a.p;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  const int my_e = lane < p.k ? a.topk_idx[(int64_t)t * p.k + lane] : -1;
+  const float g = token_gate<NJ>(p, a.logits + (int64_t)t * p.E, my_e, lane);
+  if (lane < p.k) a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -581,6 +611,9 @@ hipError_t launch_capacity_t(const CapacityArgs& a, hipStream_t s) {
   const int chunk = std::max(1, std::min(a.p.T, 15360 / (NA + a.p.k)));
   const size_t lds = sizeof(int32_t) * ((size_t)a.p.E + (size_t)chunk * NA + (size_t)chunk * a.p.k);
   hipLaunchKernelGGL((capacity_kernel<NJ>), dim3(1), dim3(kCapWaves * 64), lds, s, a, chunk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((capacity_gates_kernel<NJ>), dim3((a.p.T + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
