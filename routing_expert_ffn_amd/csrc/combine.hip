@@ -1,9 +1,10 @@
 // Gate-weighted combine of the MoE layer for gfx950:
-//   out[t] = sum_j w[t,j] * y_rows[slot_row[t,j]] + sum_s y_rows[T*k + s*T + t]
+//   out[t] = sum_j w[t,j] * y_routed[slot_row[t,j]] + sum_s y_shared[s*T + t]
 // ("15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the
 // router sketch's last line: weighted routed experts plus the shared expert).
-// One workgroup per token; 16-byte loads of the fp32 expert rows, fp32 accumulation in a
-// fixed order (slots, then shared experts), so the result is deterministic.
+// One workgroup per token; 16-byte loads of the expert rows (routed rows fp32
+// or bf16, shared rows fp32), fp32 accumulation in a fixed order (slots, then
+// shared experts), so the result is deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,7 +49,7 @@ struct Vec8<float> {
   }
 };
 
-template <typename TY, typename TO>
+template <typename TR, typename TO>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   __shared__ int32_t srow[MOE_MAX_TOPK];
   __shared__ float sw[MOE_MAX_TOPK];
@@ -58,9 +59,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     sw[threadIdx.x] = a.topk_w[(int64_t)t * a.k + threadIdx.x];
   }
   __syncthreads();
-  const TY* y = static_cast<const TY*>(a.y_rows);
+  const TR* y = static_cast<const TR*>(a.y_routed);
   TO* out = static_cast<TO*>(a.out) + (int64_t)t * a.H;
-  const int64_t shared0 = (int64_t)a.T * a.k + t;
   for (int c = threadIdx.x * 8; c < a.H; c += blockDim.x * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < a.k; ++j) {
@@ -68,13 +68,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       if (r < 0) continue;
       const float w = sw[j];
       float v[8];
-      Vec8<TY>::load(y + (int64_t)r * a.H + c, v);
+      Vec8<TR>::load(y + (int64_t)r * a.H + c, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += w * v[i];
     }
     for (int s = 0; s < a.S; ++s) {
       float v[8];
-      Vec8<TY>::load(y + (shared0 + (int64_t)s * a.T) * a.H + c, v);
+      Vec8<float>::load(a.y_shared + ((int64_t)s * a.T + t) * a.H + c, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
@@ -88,7 +88,11 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStr
   if (a.T <= 0) return hipSuccess;
   (void)dtype;  // expert rows are fp32 for every input dtype
   dim3 grid(a.T), block(256);
-  if (out_dtype == 1)
+  if (a.routed_bf16 && out_dtype == 1)
+    hipLaunchKernelGGL((combine_kernel<bf16, bf16>), grid, block, 0, s, a);
+  else if (a.routed_bf16)
+    hipLaunchKernelGGL((combine_kernel<bf16, float>), grid, block, 0, s, a);
+  else if (out_dtype == 1)
     hipLaunchKernelGGL((combine_kernel<float, bf16>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, a);

@@ -319,12 +319,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
           const float hv = g / (1.0f + __expf(-g)) * u;
           orow[nt * 128 + wc * 64 + n * 32 + (lane & 31)] = (bf16)hv;
         }
-      } else {
-        // expert outputs stay fp32 until the combine (bf16 here would put a
-        // second rounding of every expert output into the layer result)
-        float* orow = static_cast<float*>(a.c) + (int64_t)(row0 + row) * a.N;
+      } else if (a.c16 == nullptr || e >= a.n_routed) {
+        // fp32 expert rows (shared experts' rows at row - routed_rows when
+        // the routed rows go to c16)
+        const int64_t orow_i = (int64_t)(row0 + row) - (a.c16 ? a.routed_rows : 0);
+        float* orow = static_cast<float*>(a.c) + orow_i * a.N;
 #pragma unroll
         for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = acc[m][n][r];
+      } else {
+        bf16* orow = static_cast<bf16*>(a.c16) + (int64_t)(row0 + row) * a.N;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = (bf16)acc[m][n][r];
       }
     }
   }

@@ -84,11 +84,18 @@ struct GemmArgs {
   const int32_t* seg_len;
   const int32_t* f_prefix;
   const int32_t* h_prefix;
+  // down, split output: routed experts' rows (experts < n_routed, rows <
+  // routed_rows) to c16 in bf16, shared experts' rows to c (fp32) at row
+  // minus routed_rows; c16 == null: every row to c (fp32)
+  void* c16;
+  int n_routed, routed_rows;
 };
 
 struct CombineArgs {
   int T, H, k, S;
-  const void* y_rows;       // [T*k+S*T, H]
+  const void* y_routed;     // [T*k, H] routed expert rows, fp32 or bf16
+  int routed_bf16;
+  const float* y_shared;    // [S*T, H] shared expert rows (fp32)
   const int32_t* slot_row;  // [T,k]
   const float* topk_w;      // [T,k]
   void* out;                // [T,H]
