@@ -8,7 +8,8 @@ arrays into it.
 
 Inputs are numpy arrays: fp32 arrays for fp32 layers and uint16 arrays holding
 bf16 bit patterns for bf16 layers.  `cfg` is any object with the attributes
-H, E, S, k, G, topk_group, I, scoring, renorm, scale, capacity_factor, dtype.
+H, E, S, k, G, topk_group, I, scoring, renorm, scale, capacity_factor, dtype
+(and optionally drop_tokens).
 """
 import ctypes
 import os
@@ -37,7 +38,7 @@ class _Layer(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("E", ctypes.c_int32), ("S", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("G", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("scoring", ctypes.c_int32), ("renorm", ctypes.c_int32), ("scale", ctypes.c_double),
-                ("capacity_factor", ctypes.c_double), ("dtype", ctypes.c_int32)]
+                ("capacity_factor", ctypes.c_double), ("dtype", ctypes.c_int32), ("drop_tokens", ctypes.c_int32)]
 
 
 _lib_override = None
@@ -86,7 +87,8 @@ def _load():
 def _layer(cfg) -> _Layer:
     return _Layer(cfg.H, cfg.E, cfg.S, cfg.k, cfg.G, cfg.topk_group, cfg.I,
                   1 if cfg.scoring == "sigmoid" else 0, 1 if cfg.renorm else 0, float(cfg.scale),
-                  float(cfg.capacity_factor), 0 if cfg.dtype == "f32" else 1)
+                  float(cfg.capacity_factor), 0 if cfg.dtype == "f32" else 1,
+                  1 if getattr(cfg, "drop_tokens", False) else 0)
 
 
 def _ptr(a):

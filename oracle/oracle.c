@@ -31,6 +31,12 @@
  *    first served in index order, each taking its best-ranked allowed experts
  *    that still have room; slots left empty get index -1 and gate 0; groups
  *    are not re-chosen after overflow; gates are computed on the final set;
+ *  - drop mode (the same page's serving configuration, section 4.2:
+ *    drop_tokens, "drop the token when over capacity, no downgrade"): each
+ *    token keeps its top-k and the gates of that top-k; in token order a
+ *    (token, expert) assignment is kept while the expert holds fewer than C
+ *    tokens, else it is dropped (index -1, gate 0, no other expert instead,
+ *    the other gates unchanged);
  *  - shared expert s for token t lives at row T*k + s*T + t of the row space.
  *
  * Arithmetic: every dot product, activation, gate and sum is evaluated in
@@ -49,6 +55,7 @@ typedef struct {
   double scale;             /* routed scaling factor                          */
   double capacity_factor;   /* <= 0 : no capacity limit                       */
   int32_t dtype;            /* 0 = fp32 inputs, 1 = bf16 inputs (bit patterns) */
+  int32_t drop_tokens;      /* with a capacity: 1 = drop overflow, 0 = re-route */
 } oracle_layer;
 
 /* ---- input access --------------------------------------------------------- */
@@ -265,6 +272,30 @@ int oracle_select(const oracle_layer* L, int64_t T, const float* logits, const f
       for (int j = 0; j < k; ++j) idx[t * k + j] = j < n ? order[j] : -1;
       token_gates(L, logits + t * E, idx + t * k, w + t * k);
     }
+  } else if (L->drop_tokens) {
+    /* the top-k and its gates as without a limit, then, token by token, an
+     * assignment to an expert that already holds C tokens is dropped */
+    int64_t* count = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    float* score = (float*)malloc(sizeof(float) * (size_t)E);
+    int* order = (int*)malloc(sizeof(int) * (size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+      int n = token_ranking(L, logits + t * E, sel_bias, score, order, margin ? margin + t : NULL);
+      for (int j = 0; j < k; ++j) idx[t * k + j] = j < n ? order[j] : -1;
+      token_gates(L, logits + t * E, idx + t * k, w + t * k);
+      for (int j = 0; j < k; ++j) {
+        int e = idx[t * k + j];
+        if (e < 0) continue;
+        if (count[e] < cap) {
+          count[e] += 1;
+        } else {
+          idx[t * k + j] = -1;
+          w[t * k + j] = 0.0;
+        }
+      }
+    }
+    free(count);
+    free(score);
+    free(order);
   } else {
     int64_t* count = (int64_t*)calloc((size_t)E, sizeof(int64_t));
     float* score = (float*)malloc(sizeof(float) * (size_t)E);

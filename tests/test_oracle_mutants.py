@@ -30,7 +30,13 @@ MUTANTS = {
                                    "acc += elem(wd, L->dtype, i * H + n) * hbuf[i];"),
     "shared expert not added": ("for (int64_t n = 0; n < H; ++n) o[n] += y[n];",
                                 "for (int64_t n = 0; n < H; ++n) o[n] += 0.0 * y[n];"),
-    "capacity off by one": ("if (count[e] < cap) {", "if (count[e] <= cap) {"),
+    "capacity off by one": ("if (count[e] < cap) {\n          idx[t * k + got++] = e;",
+                            "if (count[e] <= cap) {\n          idx[t * k + got++] = e;"),
+    "drop mode re-routes the overflow": ("  } else if (L->drop_tokens) {", "  } else if (0) {"),
+    "drop mode lets one token too many in": ("if (count[e] < cap) {\n          count[e] += 1;",
+                                             "if (count[e] <= cap) {\n          count[e] += 1;"),
+    "drop mode keeps the dropped gate": ("idx[t * k + j] = -1;\n          w[t * k + j] = 0.0;",
+                                         "idx[t * k + j] = -1;"),
     "unnormalised softmax over the selection": ("w[j] = (L->renorm ? p / z_sel : p / z_all) * L->scale;",
                                                 "w[j] = (L->renorm ? p / z_sel : p / z_sel) * L->scale;"),
     "strided groups": ("if (kept[e / gsz]) order[n_allowed++] = e;", "if (kept[e % G]) order[n_allowed++] = e;"),
@@ -53,6 +59,8 @@ PINS = [
     S.test_softmax_gates_closed_form, S.test_ties_go_to_lower_index, S.test_softmax_gates_match_library_softmax,
     S.test_v3_gates_sum_to_scaling_factor, S.test_router_logits_are_the_fp32_rounded_matmul_plus_bias,
     lambda: S.test_capacity_matches_sequential_simulation(8, 1, 1, 2, 1.0, "softmax"),
+    S.test_drop_mode_hand_example,
+    lambda: S.test_drop_mode_is_the_unlimited_top_k_minus_late_assignments(8, 1, 1, 2, 0.75, "softmax"),
     lambda: S.test_selection_matches_exhaustive_enumeration(16, 4, 2, 3, "sigmoid"),
     P.test_hand_example,
     F.test_swiglu_closed_form_with_selection_matrices, F.test_single_expert_layer_is_a_dense_swiglu_ffn,

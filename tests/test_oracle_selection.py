@@ -311,6 +311,76 @@ def test_capacity_defining_property_v3_decode_shape():
     assert np.array_equal(load, counts)
 
 
+# ---- capacity, drop mode ---------------------------------------------------------
+# The serving configuration of "GPT-4 Has 1.8 Trillion Parameters. It Uses 2%
+# of Them Per Token" (section 4.2, drop_tokens): an assignment beyond an
+# expert's capacity is dropped instead of going to another expert.
+
+def test_drop_mode_hand_example():
+    # 4 experts, top-2, softmax; C = ceil(0.5 * 3 * 2 / 4) = 1
+    cfg = shape(T=3, E=4, k=2, capacity_factor=0.5, drop_tokens=True)
+    assert oracle.capacity(cfg, 3) == 1
+    logits = np.array([[3, 2, 0, -1],     # top-2 {0, 1}: both kept
+                       [3, -1, 2, 0],     # top-2 {0, 2}: 0 is full -> dropped, 2 kept
+                       [-1, 3, 2, 0]],    # top-2 {1, 2}: both full -> both dropped
+                      np.float32)
+    idx, w, _, counts = oracle.select(cfg, logits, None)
+    assert idx.tolist() == [[0, 1], [-1, 2], [-1, -1]]
+    assert counts.tolist() == [1, 1, 1, 0]
+    # kept gates are those of the full top-2 (renormalised softmax over the pair)
+    e2 = math.exp(2.0) / (math.exp(3.0) + math.exp(2.0))
+    np.testing.assert_allclose(w, [[1 - e2, e2], [0.0, e2], [0.0, 0.0]], rtol=1e-12)
+    # re-route mode on the same logits sends the overflow to the next-best expert
+    idx_r, _, _, _ = oracle.select(cfg.with_(drop_tokens=False), logits, None)
+    assert idx_r.tolist() == [[0, 1], [2, 3], [-1, -1]]
+
+
+@pytest.mark.parametrize("E,G,keep,k,cf,scoring", [
+    (8, 1, 1, 2, 0.75, "softmax"),
+    (16, 4, 2, 3, 1.0, "sigmoid"),
+    (256, 8, 4, 8, 1.25, "sigmoid"),
+])
+def test_drop_mode_is_the_unlimited_top_k_minus_late_assignments(E, G, keep, k, cf, scoring):
+    """Defining property, by prefix counts instead of a running counter: an
+    assignment (t, e) of the unlimited top-k survives iff fewer than C earlier
+    tokens chose e; survivors keep their unlimited gates, the rest are -1/0."""
+    rng = np.random.default_rng(E * k)
+    T = 128
+    cfg = shape(T=T, E=E, G=G, topk_group=keep, k=k, capacity_factor=cf, scoring=scoring, drop_tokens=True,
+                scale=2.5 if scoring == "sigmoid" else 1.0)
+    logits = (rng.standard_normal((T, E)) + np.linspace(2, -2, E)).astype(np.float32)
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32) if scoring == "sigmoid" else None
+    idx, w, _, counts = oracle.select(cfg, logits, bias)
+    free_idx, free_w, _, _ = oracle.select(cfg.with_(capacity_factor=0.0, drop_tokens=False), logits, bias)
+    C = oracle.capacity(cfg, T)
+    onehot = np.zeros((T, E), int)
+    for t in range(T):
+        onehot[t, free_idx[t]] = 1
+    earlier = np.cumsum(onehot, axis=0) - onehot          # selections of e by tokens before t
+    for t in range(T):
+        for j in range(k):
+            e = free_idx[t, j]
+            if earlier[t, e] < C:
+                assert idx[t, j] == e and w[t, j] == free_w[t, j]
+            else:
+                assert idx[t, j] == -1 and w[t, j] == 0.0
+    assert np.array_equal(counts, np.minimum(onehot.sum(0), C))
+
+
+def test_drop_mode_with_room_for_everyone_is_unlimited_routing():
+    rng = np.random.default_rng(3)
+    T, E = 64, 16
+    cfg = shape(T=T, E=E, G=4, topk_group=2, k=4, scoring="sigmoid", scale=2.5, capacity_factor=8.0,
+                drop_tokens=True)
+    assert oracle.capacity(cfg, T) >= T
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    a = oracle.select(cfg, logits, bias)
+    b = oracle.select(cfg.with_(capacity_factor=0.0, drop_tokens=False), logits, bias)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
 def test_margin_of_hand_built_vector():
     # kept groups 1 and 2; group margin = GS(2) - GS(0), expert margin = s(2) - s(1.5)
     cfg = shape(E=16, G=4, topk_group=2, k=2, scoring="sigmoid", renorm=True, scale=2.5)

@@ -21,6 +21,7 @@ class LayerShape:
     renorm: bool = True         # renormalise the selected gates
     scale: float = 1.0          # routed scaling factor applied to the gates
     capacity_factor: float = 0.0  # <= 0: unlimited
+    drop_tokens: bool = False   # with a capacity: drop overflow instead of re-routing
     dtype: str = "bf16"         # "bf16" | "f32" for x and every weight
     sel_bias: Optional[float] = None   # selection bias ~ U(-a, a) when set
     zipf_s: Optional[float] = None     # Zipf exponent of the per-expert logit offset
