@@ -68,11 +68,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Layer description: the fields the DeepSeek page reads from a checkpoint's
  * config (n_routed_experts, n_shared_experts, num_experts_per_tok, n_group,
  * topk_group, moe_intermediate_size, routed_scaling_factor, scoring
- * function) plus the capacity factor of the capacity passage. */
+ * function) plus the capacity factor of the capacity passage and the
+ * drop_tokens switch of the GPT-4 page's serving configuration. */
 typedef struct moe_config {
   int32_t hidden_size;           /* H; bf16 needs H % 256 == 0, f32 H % 32 == 0 */
   int32_t n_routed_experts;      /* E, 1..512                                     */
-  int32_t n_shared_experts;      /* S >= 0, each shaped like a routed expert     */
+  int32_t n_shared_experts;      /* S, 0..64, each shaped like a routed expert   */
   int32_t top_k;                 /* k, 1..min(E, 32)                              */
   int32_t n_group;               /* G >= 1, E % G == 0, E/G >= 2 when G > 1      */
   int32_t topk_group;            /* 1..G, top_k <= topk_group * E / G            */
@@ -83,6 +84,8 @@ typedef struct moe_config {
   float capacity_factor;         /* <= 0: unlimited; else C = ceil(cf*T*k/E)    */
   int32_t dtype;                 /* moe_dtype of x and every weight              */
   int32_t out_dtype;             /* moe_dtype of `out`                            */
+  int32_t drop_tokens;           /* with a capacity: 1 = drop the overflow, 0 =
+                                    re-route it to the next-best allowed expert */
 } moe_config;
 
 /* Bytes of workspace every call below needs for this layer and T tokens
@@ -109,7 +112,11 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
  * 0x1.111112p-7, 0x1.6c16c2p-10, 0x1.a01a02p-13}.  Group score = fl32(best +
  * second best) of a group's c.  Ties rank the lower index first.
  * Capacity: tokens in index order each take their best-ranked allowed experts
- * with fewer than C tokens so far; C = ceil(((cf*T)*k)/E) in double.
+ * with fewer than C tokens so far; C = ceil(((cf*T)*k)/E) in double.  With
+ * drop_tokens (the serving configuration of "GPT-4 Has 1.8 Trillion
+ * Parameters ...", section 4.2) each token keeps its top-k and their gates,
+ * and in token order an assignment whose expert already holds C tokens is
+ * dropped (index -1, gate 0) instead of going to another expert.
  * Workspace: required (MOE_ERR_WORKSPACE otherwise) with a capacity limit and
  * for bf16 layers that compute their logits; fp32 layers and logits_in
  * routing without a capacity limit may pass ws = NULL. */

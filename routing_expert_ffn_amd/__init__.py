@@ -35,17 +35,19 @@ class moe_config(ctypes.Structure):
                 ("topk_group", ctypes.c_int32), ("moe_intermediate_size", ctypes.c_int32),
                 ("scoring", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("capacity_factor", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("drop_tokens", ctypes.c_int32)]
 
 
 def make_config(shape, out_dtype=None):
     """moe_config from a layer description (attributes H, E, S, k, G,
-    topk_group, I, scoring, renorm, scale, capacity_factor, dtype)."""
+    topk_group, I, scoring, renorm, scale, capacity_factor, dtype and
+    optionally drop_tokens)."""
     dt = MOE_F32 if shape.dtype == "f32" else MOE_BF16
     od = dt if out_dtype is None else (MOE_F32 if out_dtype in ("f32", torch.float32, MOE_F32) else MOE_BF16)
     return moe_config(shape.H, shape.E, shape.S, shape.k, shape.G, shape.topk_group, shape.I,
                       MOE_SCORE_SIGMOID if shape.scoring == "sigmoid" else MOE_SCORE_SOFTMAX,
-                      1 if shape.renorm else 0, float(shape.scale), float(shape.capacity_factor), dt, od)
+                      1 if shape.renorm else 0, float(shape.scale), float(shape.capacity_factor), dt, od,
+                      1 if getattr(shape, "drop_tokens", False) else 0)
 
 
 _lib = None

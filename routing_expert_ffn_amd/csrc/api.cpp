@@ -53,6 +53,7 @@ struct Dims {
   int H, E, S, k, G, gsz, topk_group, I, scoring, renorm, dtype, out_dtype;
   float scale;
   int capacity;   // <= 0: unlimited
+  int drop;       // with a capacity: drop the overflow instead of re-routing
   int n_allowed;
   int esz;        // bytes per input element
 };
@@ -104,6 +105,8 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
   const int64_t rows = T * d.k + (int64_t)d.S * T;
   if (rows > 0x7FFFFFFF || T * (int64_t)d.E > 0x7FFFFFFF)
     return fail(MOE_ERR_UNSUPPORTED, "T*(k+S) and T*E must fit in int32");
+  if (c->drop_tokens != 0 && c->drop_tokens != 1) return fail(MOE_ERR_INVALID_ARG, "drop_tokens must be 0 or 1");
+  d.drop = c->drop_tokens;
   d.capacity = 0;
   if (c->capacity_factor > 0.0f) {
     // C = ceil(((cf*T)*k)/E) evaluated in IEEE double, left to right
@@ -139,7 +142,7 @@ Layout layout_of(const Dims& d) {
     nsplit = (size_t)router_splits(d.T, d.H, &sps);
   }
   L.rpart = take(nsplit > 1 ? nsplit * T * E * 4 : 0);
-  L.cand = take(d.capacity > 0 ? T * (size_t)d.n_allowed * 4 : 0);
+  L.cand = take(d.capacity > 0 && !d.drop ? T * (size_t)d.n_allowed * 4 : 0);
   L.idx = take(T * k * 4);
   L.w = take(T * k * 4);
   L.counts = take(E * 4);
@@ -237,6 +240,28 @@ moe_status do_route(const Dims& d, const void* x, const void* w_router, const fl
   a.topk_w = topk_w;
   a.counts = nullptr;
   hipError_t e;
+  if (d.capacity > 0 && d.drop) {
+    // drop mode: unlimited top-k and gates, then the capacity pass drops
+    // late assignments in place
+    a.p.capacity = 0;
+    if (logits_in && logits_out) {
+      e = hipMemcpyAsync(logits_out, logits_in, sizeof(float) * d.T * d.E, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "logits copy");
+      a.logits_out = nullptr;
+    }
+    e = run_router(d, a, x, w_router, ws, L, s);
+    if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+    CapacityArgs c{};
+    c.p = route_params(d);
+    c.drop = 1;
+    c.cand = topk_idx;
+    c.topk_idx = topk_idx;
+    c.topk_w = topk_w;
+    c.counts = counts;
+    e = timed(K_CAPACITY, s, [&] { return launch_capacity(c, s); });
+    if (e != hipSuccess) return hip_fail(e, "capacity kernel launch");
+    return MOE_OK;
+  }
   if (d.capacity > 0) {
     // the capacity pass reads the logits (gates of the final selection)
     float* lg = logits_out ? logits_out : at<float>(ws, L.logits);

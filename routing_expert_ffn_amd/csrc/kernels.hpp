@@ -41,6 +41,8 @@ struct RouterGemmArgs {
 
 struct CapacityArgs {
   RouteParams p;
+  int drop;                 // 1: cand is each token's top-k (= topk_idx); an
+                            // assignment to a full expert is dropped in place
   const float* logits;      // [T,E]
   const int32_t* cand;      // [T,n_allowed]
   int32_t* topk_idx;        // [T,k]

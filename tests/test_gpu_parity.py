@@ -244,9 +244,11 @@ def test_route_ties_and_sigmoid_near_ties_from_given_logits():
     np.testing.assert_allclose(w2.cpu().numpy(), ow2, rtol=1e-5, atol=1e-6)
 
 
-@pytest.mark.parametrize("cf", [0.25, 1.25])
-def test_capacity_with_drops_and_overflow(cf):
-    shape = TEST_SHAPES["v3_decode_small"].with_(capacity_factor=cf)
+@pytest.mark.parametrize("cf,drop", [(0.25, False), (1.25, False), (0.25, True), (1.25, True)])
+def test_capacity_with_drops_and_overflow(cf, drop):
+    """Re-route mode (overflow to the next-best allowed expert) and drop mode
+    (overflow assignments dropped, the top-k's gates kept)."""
+    shape = TEST_SHAPES["v3_decode_small"].with_(capacity_factor=cf, drop_tokens=drop)
     inp = make_inputs(shape, device="cuda")
     g = run_layer(shape, inp, "f32")
     idx = g["idx"].numpy()
