@@ -31,9 +31,10 @@
  *    first served in index order, each taking its best-ranked allowed experts
  *    that still have room; slots left empty get index -1 and gate 0; groups
  *    are not re-chosen after overflow; gates are computed on the final set;
- *  - drop mode (the same page's serving configuration, section 4.2:
- *    drop_tokens, "drop the token when over capacity, no downgrade"): each
- *    token keeps its top-k and the gates of that top-k; in token order a
+ *  - drop mode (the same page's serving configuration, section 4.2: the
+ *    drop_tokens switch, overflow is dropped rather than sent to a lesser
+ *    expert): each token keeps its top-k and the gates of that top-k; in
+ *    token order a
  *    (token, expert) assignment is kept while the expert holds fewer than C
  *    tokens, else it is dropped (index -1, gate 0, no other expert instead,
  *    the other gates unchanged);
