@@ -76,6 +76,7 @@ def _load():
         lib.oracle_expert_rows.argtypes = [P, I64, P, P, P, P, P]
         lib.oracle_forward_tokens.argtypes = [P, I64, P, P, P, P, P, P, P, P]
         lib.oracle_combine.argtypes = [P, I64, P, P, P, P]
+        lib.oracle_balance_update.argtypes = [ctypes.c_int, P, P, ctypes.c_float, P, P]
         lib.oracle_moe_layer_params.restype = I64
         lib.oracle_moe_layer_params.argtypes = [I64, I64, I64, I64]
         lib.oracle_moe_active_params.restype = I64
@@ -236,6 +237,21 @@ def combine(cfg, y_rows, slot_row, w):
     L = _layer(cfg)
     _load().oracle_combine(ctypes.byref(L), T, _ptr(y_rows), _ptr(slot_row), _ptr(w), _ptr(out))
     return out
+
+
+def balance_update(counts, bias, gamma):
+    """One auxiliary-loss-free balancing step.  counts [E] int, bias [E]
+    fp32, gamma fp32 -> (new bias [E] fp32, share [E] float64, stats
+    {entropy (nats), max_share, over, under})."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    b = np.array(bias, dtype=np.float32, copy=True)
+    E = counts.shape[0]
+    share = np.empty(E, dtype=np.float64)
+    stats = np.empty(4, dtype=np.float64)
+    st = _load().oracle_balance_update(E, _ptr(counts), _ptr(b), ctypes.c_float(gamma), _ptr(share), _ptr(stats))
+    if st != 0:
+        raise ValueError("negative expert count")
+    return b, share, {"entropy": stats[0], "max_share": stats[1], "over": int(stats[2]), "under": int(stats[3])}
 
 
 def moe_layer_params(H, E, S, I):

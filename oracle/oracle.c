@@ -470,6 +470,51 @@ int oracle_combine(const oracle_layer* L, int64_t T, const double* y_rows, const
   return 0;
 }
 
+/* ---- load balancing ---------------------------------------------------------- */
+/* One step of the auxiliary-loss-free balancing ("15. DeepSeek：MLA、MoE 与 MTP",
+ * section "V3 的 MoE：256 个专家怎样选 8 个", the paragraph on the bias): an
+ * expert that received more tokens than the mean over the experts has its
+ * selection bias lowered by gamma, one that received fewer has it raised, one
+ * exactly at the mean keeps it (reading: the page names only overloaded and
+ * idle experts).  The bias is fp32 state, so the step is one fp32 rounding:
+ * b <- fl32(b - gamma) or fl32(b + gamma).  The mean test is exact integer
+ * arithmetic: n_e > N/E  <=>  n_e * E > N.
+ * Load telemetry (the same section's monitoring paragraph; the expert-call
+ * entropy of "GPT-4 Has 1.8 Trillion Parameters ...", section 4.4):
+ * share[e] = n_e / N, stats = {entropy -sum share*ln(share) in nats (0*ln 0 =
+ * 0), largest share, experts above the mean, experts below the mean}.  N == 0:
+ * no update, shares 0, entropy 0. */
+int oracle_balance_update(int E, const int32_t* counts, float* bias, float gamma, double* share, double* stats) {
+  int64_t N = 0;
+  for (int e = 0; e < E; ++e) {
+    if (counts[e] < 0) return -1;
+    N += counts[e];
+  }
+  double ent = 0.0, mx = 0.0;
+  int over = 0, under = 0;
+  for (int e = 0; e < E; ++e) {
+    const int64_t scaled = (int64_t)counts[e] * E;
+    if (N > 0 && scaled > N) {
+      bias[e] = bias[e] - gamma;
+      over += 1;
+    } else if (N > 0 && scaled < N) {
+      bias[e] = bias[e] + gamma;
+      under += 1;
+    }
+    const double p = N > 0 ? (double)counts[e] / (double)N : 0.0;
+    if (share) share[e] = p;
+    if (p > 0.0) ent -= p * log(p);
+    if (p > mx) mx = p;
+  }
+  if (stats) {
+    stats[0] = ent;
+    stats[1] = mx;
+    stats[2] = over;
+    stats[3] = under;
+  }
+  return 0;
+}
+
 /* ---- parameter arithmetic ---------------------------------------------------- */
 /* One MoE layer: router E*H plus (E+S) experts of three H x I matrices. */
 int64_t oracle_moe_layer_params(int64_t H, int64_t E, int64_t S, int64_t I) { return E * H + (E + S) * 3 * H * I; }

@@ -11,6 +11,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_balance as B
 from tests import test_oracle_ffn as F
 from tests import test_oracle_permute as P
 from tests import test_oracle_selection as S
@@ -48,6 +49,9 @@ MUTANTS = {
                                              "for (int i = 0; i <= L->topk_group && i < G; ++i) kept[gid[i]] = 1;"),
     "permutation in descending token order": ("for (int e = 0; e < E; ++e) fill[e] = offsets[e];\n  for (int64_t t = 0; t < T; ++t) {",
                                               "for (int e = 0; e < E; ++e) fill[e] = offsets[e];\n  for (int64_t t = T - 1; t >= 0; --t) {"),
+    "balancing pushes experts at the mean": ("if (N > 0 && scaled > N) {", "if (N > 0 && scaled >= N) {"),
+    "balancing with the sign reversed": ("bias[e] = bias[e] - gamma;", "bias[e] = bias[e] + gamma;"),
+    "entropy in bits": ("if (p > 0.0) ent -= p * log(p);", "if (p > 0.0) ent -= p * log2(p);"),
     "expert gate weight ignored": ("for (int64_t n = 0; n < H; ++n) o[n] += w[t * k + j] * y[n];",
                                    "for (int64_t n = 0; n < H; ++n) o[n] += y[n];"),
 }
@@ -63,6 +67,7 @@ PINS = [
     lambda: S.test_drop_mode_is_the_unlimited_top_k_minus_late_assignments(8, 1, 1, 2, 0.75, "softmax"),
     lambda: S.test_selection_matches_exhaustive_enumeration(16, 4, 2, 3, "sigmoid"),
     P.test_hand_example,
+    B.test_loads_at_the_mean_keep_their_bias, B.test_random_loads_against_library_entropy_and_float32_steps,
     F.test_swiglu_closed_form_with_selection_matrices, F.test_single_expert_layer_is_a_dense_swiglu_ffn,
     F.test_identical_experts_factor_out, F.test_empty_slots_are_skipped_and_bf16_inputs_are_exact,
 ]
