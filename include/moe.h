@@ -164,6 +164,24 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
                        const void* w_down, void* out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
                        float* logits_out, void* ws, size_t ws_bytes, void* stream);
 
+/* One step of auxiliary-loss-free load balancing ("15. DeepSeek：MLA、MoE 与
+ * MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the bias paragraph) and the
+ * load telemetry of its monitoring paragraph (plus the expert-call entropy of
+ * "GPT-4 Has 1.8 Trillion Parameters ...", section 4.4).
+ *   expert_counts [E] int32, e.g. from moe_route / moe_forward (N = their sum)
+ *   sel_bias      [E] fp32, updated in place, or NULL (telemetry only): an
+ *                 expert with n_e > N/E gets fl32(b - gamma), one with
+ *                 n_e < N/E gets fl32(b + gamma), one at the mean keeps b
+ *                 (the test is exact: n_e * E against N); N == 0: no change
+ *   gamma         the step, >= 0 (the page uses 0.001)
+ *   share         [E] fp32 out, n_e / N (0 when N == 0), or NULL
+ *   stats         [4] fp32 out, or NULL: entropy of the shares in nats
+ *                 (0 ln 0 = 0), largest share, experts above the mean,
+ *                 experts below the mean
+ * Only cfg's expert count is used.  Deterministic (fixed-order reductions). */
+moe_status moe_balance_update(const moe_config* cfg, const int32_t* expert_counts, float* sel_bias, float gamma,
+                              float* share, float* stats, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* moe_last_error(void);
 

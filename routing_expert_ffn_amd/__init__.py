@@ -20,7 +20,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
           -4: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_last_error", "moe_version", "moe_timing_enable", "moe_timing_read", "moe_kernel_name")
+           "moe_balance_update", "moe_last_error", "moe_version", "moe_timing_enable", "moe_timing_read",
+           "moe_kernel_name")
 
 
 class MoeError(RuntimeError):
@@ -65,13 +66,14 @@ def lib():
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         C = ctypes.POINTER(moe_config)
         for name in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-                     "moe_forward", "moe_timing_enable", "moe_timing_read"):
+                     "moe_forward", "moe_balance_update", "moe_timing_enable", "moe_timing_read"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [C, I64, ctypes.POINTER(SZ)]
         L.moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_permute.argtypes = [C, I64, P, P, P, P, P, P, SZ, P]
         L.moe_expert_ffn.argtypes = [C, I64, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_combine.argtypes = [C, I64, P, P, P, P, P]
+        L.moe_balance_update.argtypes = [C, P, P, ctypes.c_float, P, P, P]
         L.moe_forward.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
@@ -171,6 +173,18 @@ def combine(cfg, T, y_rows, slot_row, topk_w, out=None, stream=None):
     _check(lib().moe_combine(ctypes.byref(cfg), T, _p(y_rows), _p(slot_row), _p(topk_w), _p(out),
                              _stream(stream)))
     return out
+
+
+def balance_update(cfg, expert_counts, sel_bias=None, gamma=0.001, stream=None):
+    """One auxiliary-loss-free balancing step: sel_bias [E] fp32 is updated in
+    place (if given); -> (share [E] fp32, stats [4] fp32: entropy in nats,
+    max share, experts above / below the mean load)."""
+    dev = expert_counts.device
+    share = torch.empty(cfg.n_routed_experts, dtype=torch.float32, device=dev)
+    stats = torch.empty(4, dtype=torch.float32, device=dev)
+    _check(lib().moe_balance_update(ctypes.byref(cfg), _p(expert_counts), _p(sel_bias), float(gamma), _p(share),
+                                    _p(stats), _stream(stream)))
+    return share, stats
 
 
 def forward(cfg, x, w_router, w_gate, w_up, w_down, logit_bias=None, sel_bias=None, out=None, topk_idx=None,

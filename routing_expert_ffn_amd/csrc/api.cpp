@@ -407,7 +407,7 @@ moe_status do_combine(const Dims& d, const void* y_routed, bool routed_bf16, con
 const char* kernel_name(int id) {
   static const char* names[K_COUNT] = {"fill",          "router",          "router_select", "capacity",
                                        "permute_count", "permute_scan",    "permute_scatter", "schedule",
-                                       "gateup_swiglu", "down",            "combine"};
+                                       "gateup_swiglu", "down",            "combine",         "balance"};
   return (id >= 0 && id < K_COUNT) ? names[id] : nullptr;
 }
 
@@ -539,6 +539,26 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
   st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y, ws, L, s);
   if (st != MOE_OK) return st;
   return do_combine(d, y, false, static_cast<const float*>(y) + (int64_t)d.T * d.k * d.H, slot_row, w, out, s);
+}
+
+moe_status moe_balance_update(const moe_config* cfg, const int32_t* expert_counts, float* sel_bias, float gamma,
+                              float* share, float* stats, void* stream) {
+  Dims d;
+  moe_status st = check_config(cfg, 0, d);
+  if (st != MOE_OK) return st;
+  if (!expert_counts) return fail(MOE_ERR_INVALID_ARG, "expert_counts is required");
+  if (!(gamma >= 0.0f) || gamma == INFINITY) return fail(MOE_ERR_INVALID_ARG, "gamma must be finite and >= 0");
+  BalanceArgs a{};
+  a.E = d.E;
+  a.counts = expert_counts;
+  a.bias = sel_bias;
+  a.gamma = gamma;
+  a.share = share;
+  a.stats = stats;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(K_BALANCE, s, [&] { return launch_balance(a, s); });
+  if (e != hipSuccess) return hip_fail(e, "balance kernel launch");
+  return MOE_OK;
 }
 
 const char* moe_last_error(void) { return g_err.c_str(); }

@@ -103,6 +103,16 @@ struct CombineArgs {
   void* out;                // [T,H]
 };
 
+// One balancing step (selection bias) and the load telemetry.
+struct BalanceArgs {
+  int E;
+  const int32_t* counts;    // [E]
+  float* bias;              // [E] selection bias, updated in place, or null
+  float gamma;
+  float* share;             // [E] or null
+  float* stats;             // [4] or null: entropy (nats), max share, experts above / below the mean
+};
+
 // Kernel ids (for timing); names in kernel_names().
 enum KernelId {
   K_FILL = 0,
@@ -116,6 +126,7 @@ enum KernelId {
   K_GATEUP,
   K_DOWN,
   K_COMBINE,
+  K_BALANCE,
   K_COUNT
 };
 
@@ -141,4 +152,5 @@ int gemm_bm(int dtype);
 int gemm_half_rows(int dtype);
 hipError_t launch_gateup(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStream_t s);
+hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s);

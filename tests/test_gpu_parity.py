@@ -357,3 +357,36 @@ def test_expert_ffn_row_tile_boundaries():
         rms = np.sqrt(np.mean(ref ** 2))
         err = np.max(np.abs(yh[rows] - ref))
         assert err <= 2e-2 * rms, (e, counts[e] if e < E else T, err / rms)
+
+
+# ---- auxiliary-loss-free balancing step -------------------------------------------
+
+@pytest.mark.parametrize("case", ["forward_counts", "random", "at_mean", "empty"])
+def test_balance_update_matches_oracle(case):
+    shape = TEST_SHAPES["v3_small"]
+    cfg = moe.make_config(shape)
+    E = shape.E
+    rng = np.random.default_rng(17)
+    if case == "forward_counts":
+        inp = make_inputs(shape, device="cuda")
+        g = run_layer(shape, inp, "f32")
+        counts = g["counts"].numpy().astype(np.int32)
+    elif case == "random":
+        counts = rng.poisson(40, E).astype(np.int32)
+        counts[:7] = 0
+    elif case == "at_mean":
+        counts = np.full(E, 9, np.int32)
+        counts[0], counts[1] = 12, 6          # the mean stays 9
+    else:
+        counts = np.zeros(E, np.int32)
+    b0 = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    bias = torch.from_numpy(b0.copy()).cuda()
+    share, stats = moe.balance_update(cfg, torch.from_numpy(counts).cuda(), bias, 0.001)
+    torch.cuda.synchronize()
+    ob, oshare, ost = oracle.balance_update(counts, b0, 0.001)
+    assert np.array_equal(bias.cpu().numpy(), ob)                     # the fp32 step is exact
+    np.testing.assert_allclose(share.cpu().numpy(), oshare, rtol=1e-7, atol=0)
+    st = stats.cpu().numpy()
+    np.testing.assert_allclose(st[0], ost["entropy"], rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(st[1], ost["max_share"], rtol=1e-7)
+    assert int(st[2]) == ost["over"] and int(st[3]) == ost["under"]
