@@ -68,6 +68,10 @@ def _load():
         lib.oracle_sigmoid32.argtypes = [ctypes.c_float]
         lib.oracle_sigmoid32_array.argtypes = [I64, P, P]
         lib.oracle_exp32_array.argtypes = [I64, P, P]
+        lib.oracle_sqrtsoftplus32.restype = ctypes.c_float
+        lib.oracle_sqrtsoftplus32.argtypes = [ctypes.c_float]
+        lib.oracle_sqrtsoftplus32_array.argtypes = [I64, P, P]
+        lib.oracle_hash_select.argtypes = [P, I64, P, P, P, I64, P, P, P]
         lib.oracle_router_logits.argtypes = [P, I64, P, P, P, P]
         lib.oracle_select.argtypes = [P, I64, P, P, P, P, P, P]
         lib.oracle_capacity.restype = I64
@@ -85,9 +89,12 @@ def _load():
     return _lib
 
 
+_SCORING = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
+
+
 def _layer(cfg) -> _Layer:
     return _Layer(cfg.H, cfg.E, cfg.S, cfg.k, cfg.G, cfg.topk_group, cfg.I,
-                  1 if cfg.scoring == "sigmoid" else 0, 1 if cfg.renorm else 0, float(cfg.scale),
+                  _SCORING[cfg.scoring], 1 if cfg.renorm else 0, float(cfg.scale),
                   float(cfg.capacity_factor), 0 if cfg.dtype == "f32" else 1,
                   1 if getattr(cfg, "drop_tokens", False) else 0)
 
@@ -123,6 +130,13 @@ def sigmoid32(l):
     return out
 
 
+def sqrtsoftplus32(l):
+    l = np.ascontiguousarray(l, dtype=np.float32)
+    out = np.empty_like(l)
+    _load().oracle_sqrtsoftplus32_array(l.size, _ptr(l), _ptr(out))
+    return out
+
+
 def router_logits(cfg, x, w_router, logit_bias=None):
     x = _input(x, cfg)
     w_router = _input(w_router, cfg)
@@ -155,6 +169,29 @@ def select(cfg, logits, sel_bias=None):
     if rc != 0:
         raise ValueError("oracle_select rejected the layer shape")
     return idx, w, margin, counts
+
+
+def hash_select(cfg, logits, token_ids, tid2eid):
+    """Hash routing: experts from rows of the table tid2eid [vocab, k] picked
+    by token_ids [T]; gates from the logits.  -> (idx int32 [T,k], w float64
+    [T,k], counts int32 [E])"""
+    logits = _f32(logits)
+    T = logits.shape[0]
+    token_ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+    tid2eid = np.ascontiguousarray(tid2eid, dtype=np.int32)
+    if token_ids.shape != (T,) or tid2eid.ndim != 2 or tid2eid.shape[1] != cfg.k:
+        raise ValueError("token_ids must be [T] and tid2eid [vocab, k]")
+    idx = np.empty((T, cfg.k), dtype=np.int32)
+    w = np.empty((T, cfg.k), dtype=np.float64)
+    counts = np.empty((cfg.E,), dtype=np.int32)
+    L = _layer(cfg)
+    rc = _load().oracle_hash_select(ctypes.byref(L), T, _ptr(logits), _ptr(token_ids), _ptr(tid2eid),
+                                    tid2eid.shape[0], _ptr(idx), _ptr(w), _ptr(counts))
+    if rc == -2:
+        raise ValueError("hash routing has no next-best expert: capacity needs drop mode")
+    if rc != 0:
+        raise ValueError("oracle_hash_select rejected the layer shape")
+    return idx, w, counts
 
 
 def permute(cfg, idx):
@@ -213,12 +250,18 @@ def forward_tokens(cfg, tokens, x, idx, w, get_expert):
     return out
 
 
-def forward(cfg, x, w_router, w_gate, w_up, w_down, sel_bias=None, logit_bias=None, tokens=None):
+def forward(cfg, x, w_router, w_gate, w_up, w_down, sel_bias=None, logit_bias=None, tokens=None,
+            token_ids=None, tid2eid=None):
     """Whole layer: logits -> selection -> experts -> combine.  Returns a dict
     with logits, idx, w, margin, counts and out (float64, rows of `tokens`,
-    all tokens by default)."""
+    all tokens by default).  With token_ids and tid2eid the selection is hash
+    routing (margin is then +inf: no ranking decides it)."""
     logits = router_logits(cfg, x, w_router, logit_bias)
-    idx, w, margin, counts = select(cfg, logits, sel_bias)
+    if tid2eid is not None:
+        idx, w, counts = hash_select(cfg, logits, token_ids, tid2eid)
+        margin = np.full(logits.shape[0], np.inf)
+    else:
+        idx, w, margin, counts = select(cfg, logits, sel_bias)
     T = x.shape[0]
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     out = forward_tokens(cfg, tokens, x, idx, w, lambda e: (w_gate[e], w_up[e], w_down[e]))

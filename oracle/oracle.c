@@ -21,6 +21,11 @@
  *  - same DeepSeek page, section "671B 和 37B 的参数账": an expert is three
  *    H x I matrices (gate, up, down); the router is E x H.
  *  - "MoE on KnightLi的博客", activation-function section: SwiGLU expert FFN.
+ *  - same DeepSeek page, section "V4：放弃潜向量，改用压缩注意力", the FFN
+ *    paragraph, and the page's table of generations: V4 scores with
+ *    sqrt(softplus(l)) plus the selection bias and no group limit, and its
+ *    first layers choose experts by a fixed token-id table (tid2eid) with the
+ *    router only weighting them.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - ties in every ranking are broken by the lower index;
@@ -38,6 +43,16 @@
  *    (token, expert) assignment is kept while the expert holds fewer than C
  *    tokens, else it is dropped (index -1, gate 0, no other expert instead,
  *    the other gates unchanged);
+ *  - sqrt(softplus) scoring (same DeepSeek page, V4 section: softplus, then a
+ *    square root, in place of the sigmoid, with the selection bias and no
+ *    group limit): selected on the fp32 function sqrtsoftplus32 below, gates
+ *    from the unbiased fp64 value renormalised over the chosen experts and
+ *    scaled, as for sigmoid scoring;
+ *  - hash routing (same section: a fixed token-id -> experts table chooses,
+ *    the router only weights): an id outside the table chooses nothing, a
+ *    table entry outside [0, E) or repeating an earlier entry of its row
+ *    leaves its slot empty, the gates are those of the configured scoring
+ *    over the table's experts, and a capacity limit can only drop;
  *  - shared expert s for token t lives at row T*k + s*T + t of the row space.
  *
  * Arithmetic: every dot product, activation, gate and sum is evaluated in
@@ -51,7 +66,7 @@
 
 typedef struct {
   int32_t H, E, S, k, G, topk_group, I;
-  int32_t scoring;          /* 0 = softmax, 1 = sigmoid                       */
+  int32_t scoring;          /* 0 = softmax, 1 = sigmoid, 2 = sqrt(softplus)   */
   int32_t renorm;           /* 1 = renormalise the selected gates             */
   double scale;             /* routed scaling factor                          */
   double capacity_factor;   /* <= 0 : no capacity limit                       */
@@ -121,6 +136,41 @@ void oracle_exp32_array(int64_t n, const float* in, float* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_exp32(in[i]);
 }
 
+/* ---- fp32 sqrt(softplus) used for selection ------------------------------- */
+/* log(1 + u) for 0 < u <= 1 from log(1+u) = 2 atanh(z), z = u / (2 + u) in
+ * (0, 1/3]: atanh(z) = z * sum_j w^j / (2j + 1) with w = z^2 <= 1/9, summed
+ * through the w^7 term (the first omitted term is below 2^-26 of the sum).
+ * Coefficients 1/(2j+1) rounded to fp32, Horner form with fused multiply-adds,
+ * every step one correctly rounded fp32 operation. */
+static const float LOG1P32_C[8] = {0x1p+0f,        0x1.555556p-2f, 0x1.99999ap-3f, 0x1.24924ap-3f,
+                                   0x1.c71c72p-4f, 0x1.745d18p-4f, 0x1.3b13b2p-4f, 0x1.111112p-4f};
+
+static float log1p32_unit(float u) {
+  float d = 2.0f + u;
+  float z = u / d;
+  float w = z * z;
+  float q = LOG1P32_C[7];
+  for (int j = 6; j >= 0; --j) q = fmaf(q, w, LOG1P32_C[j]);
+  float z2 = z + z;
+  return z2 * q;
+}
+
+/* sqrtsoftplus32(l) = sqrt(max(l, 0) + log1p32(exp32(-a))), a = min(|l|, 80):
+ * softplus(l) = max(l, 0) + log(1 + e^-|l|) keeps every intermediate normal;
+ * below l = -80 the value stays at that of -80.  The square root is the
+ * correctly rounded fp32 one. */
+float oracle_sqrtsoftplus32(float l) {
+  float a = fabsf(l);
+  if (a > 80.0f) a = 80.0f;
+  float u = oracle_exp32(-a);
+  float sp = (l > 0.0f ? l : 0.0f) + log1p32_unit(u);
+  return sqrtf(sp);
+}
+
+void oracle_sqrtsoftplus32_array(int64_t n, const float* in, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_sqrtsoftplus32(in[i]);
+}
+
 /* ---- router logits -------------------------------------------------------- */
 /* logits[t,e] = fl32( sum_h x[t,h] * w_router[e,h] + logit_bias[e] ) */
 int oracle_router_logits(const oracle_layer* L, int64_t T, const void* x, const void* w_router,
@@ -158,6 +208,14 @@ static void rank_sort(int* ids, int n, const float* v) {
 
 static double sigmoid64(double l) { return 1.0 / (1.0 + exp(-l)); }
 
+/* sqrt(softplus(l)) in double, softplus(l) = max(l, 0) + log1p(exp(-|l|)) */
+static double sqrtsoftplus64(double l) { return sqrt((l > 0.0 ? l : 0.0) + log1p(exp(-fabs(l)))); }
+
+/* unbiased score of the gates: sigmoid (scoring 1) or sqrt(softplus) (2) */
+static double gate_score64(const oracle_layer* L, float l) {
+  return L->scoring == 2 ? sqrtsoftplus64((double)l) : sigmoid64((double)l);
+}
+
 /* Per token: the selection score of each expert (fp32), the allowed set after
  * group limiting, the allowed experts in rank order, and the selection margin.
  * Returns the number of allowed experts written to `order`. */
@@ -165,8 +223,8 @@ static int token_ranking(const oracle_layer* L, const float* logit, const float*
                          int* order, double* margin) {
   const int E = L->E, G = L->G;
   for (int e = 0; e < E; ++e) {
-    if (L->scoring == 1) {
-      float s = oracle_sigmoid32(logit[e]);
+    if (L->scoring == 1 || L->scoring == 2) {
+      float s = L->scoring == 1 ? oracle_sigmoid32(logit[e]) : oracle_sqrtsoftplus32(logit[e]);
       float b = sel_bias ? sel_bias[e] : 0.0f;
       score[e] = s + b; /* fp32 addition */
     } else {
@@ -215,16 +273,16 @@ static int token_ranking(const oracle_layer* L, const float* logit, const float*
 /* Gates of one token over its final selection idx[0..k) (-1 = empty slot). */
 static void token_gates(const oracle_layer* L, const float* logit, const int32_t* idx, double* w) {
   const int k = L->k, E = L->E;
-  if (L->scoring == 1) {
+  if (L->scoring == 1 || L->scoring == 2) {
     double sum = 0.0;
     for (int j = 0; j < k; ++j)
-      if (idx[j] >= 0) sum += sigmoid64((double)logit[idx[j]]);
+      if (idx[j] >= 0) sum += gate_score64(L, logit[idx[j]]);
     for (int j = 0; j < k; ++j) {
       if (idx[j] < 0) {
         w[j] = 0.0;
         continue;
       }
-      double s = sigmoid64((double)logit[idx[j]]);
+      double s = gate_score64(L, logit[idx[j]]);
       w[j] = (L->renorm ? s / sum : s) * L->scale;
     }
   } else {
@@ -317,6 +375,56 @@ int oracle_select(const oracle_layer* L, int64_t T, const float* logits, const f
     free(count);
     free(score);
     free(order);
+  }
+  if (counts_out) {
+    memset(counts_out, 0, sizeof(int32_t) * (size_t)E);
+    for (int64_t i = 0; i < T * k; ++i)
+      if (idx[i] >= 0) counts_out[idx[i]] += 1;
+  }
+  return 0;
+}
+
+/* ---- hash routing ----------------------------------------------------------- */
+/* Experts of token t read from a fixed table: row token_ids[t] of tid2eid
+ * [vocab, k]; the logits only give the gates (token_gates over that set).
+ * An id outside [0, vocab) chooses nothing; an entry outside [0, E) or equal
+ * to an earlier entry of its row leaves its slot empty (-1, gate 0).  With a
+ * capacity limit only drop mode applies (there is no next-best expert): in
+ * token order an assignment to an expert that already holds C tokens is
+ * dropped.  Returns -2 for a re-route capacity, -1 for a bad shape. */
+int oracle_hash_select(const oracle_layer* L, int64_t T, const float* logits, const int32_t* token_ids,
+                       const int32_t* tid2eid, int64_t vocab, int32_t* idx, double* w, int32_t* counts_out) {
+  const int E = L->E, k = L->k;
+  if (E > 4096 || k < 1 || vocab < 0) return -1;
+  const int64_t cap = oracle_capacity(L, T);
+  if (cap >= 0 && !L->drop_tokens) return -2;
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t id = token_ids[t];
+    for (int j = 0; j < k; ++j) {
+      int e = -1;
+      if (id >= 0 && id < vocab) {
+        e = tid2eid[id * k + j];
+        if (e < 0 || e >= E) e = -1;
+        for (int i = 0; i < j && e >= 0; ++i)
+          if (tid2eid[id * k + i] == e) e = -1;
+      }
+      idx[t * k + j] = e;
+    }
+    token_gates(L, logits + t * E, idx + t * k, w + t * k);
+  }
+  if (cap >= 0) {
+    int64_t* held = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    for (int64_t i = 0; i < T * k; ++i) {
+      const int e = idx[i];
+      if (e < 0) continue;
+      if (held[e] >= cap) {
+        idx[i] = -1; /* the expert is full: this assignment is dropped */
+        w[i] = 0.0;
+      } else {
+        held[e] += 1;
+      }
+    }
+    free(held);
   }
   if (counts_out) {
     memset(counts_out, 0, sizeof(int32_t) * (size_t)E);

@@ -16,6 +16,7 @@ from tests import test_oracle_ffn as F
 from tests import test_oracle_permute as P
 from tests import test_oracle_selection as S
 from tests import test_oracle_sigmoid as G
+from tests import test_oracle_v4 as V
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -43,8 +44,23 @@ MUTANTS = {
     "strided groups": ("if (kept[e / gsz]) order[n_allowed++] = e;", "if (kept[e % G]) order[n_allowed++] = e;"),
     "ln2 low part dropped": ("r = fmaf(-n, EXP32_LN2_LO, r);", "r = r;"),
     "logit bias ignored": ("if (logit_bias) acc += (double)logit_bias[e];", "(void)logit_bias;"),
-    "gates from the biased score": ("double s = sigmoid64((double)logit[idx[j]]);\n      w[j]",
-                                    "double s = sigmoid64((double)logit[idx[j]]) + 0.01 * j;\n      w[j]"),
+    "gates from the biased score": ("double s = gate_score64(L, logit[idx[j]]);\n      w[j]",
+                                    "double s = gate_score64(L, logit[idx[j]]) + 0.01 * j;\n      w[j]"),
+    "log1p series not doubled": ("float z2 = z + z;", "float z2 = z;"),
+    "softplus without its linear part": ("float sp = (l > 0.0f ? l : 0.0f) + log1p32_unit(u);",
+                                         "float sp = 0.0f + log1p32_unit(u);"),
+    "sqrt(softplus) without the clamp": ("  if (a > 80.0f) a = 80.0f;\n  float u", "  float u"),
+    "sqrt(softplus) gates from the sigmoid": (
+        "return L->scoring == 2 ? sqrtsoftplus64((double)l) : sigmoid64((double)l);",
+        "return sigmoid64((double)l);"),
+    "sqrt(softplus) selection without the square root": (
+        "float s = L->scoring == 1 ? oracle_sigmoid32(logit[e]) : oracle_sqrtsoftplus32(logit[e]);",
+        "float s = L->scoring == 1 ? oracle_sigmoid32(logit[e]) : logit[e];"),
+    "hash table read transposed": ("e = tid2eid[id * k + j];", "e = tid2eid[j * vocab + id];"),
+    "hash routing keeps repeated entries": ("if (tid2eid[id * k + i] == e) e = -1;", "if (0) e = -1;"),
+    "hash routing reads negative ids as row 0": ("const int64_t id = token_ids[t];",
+                                                 "const int64_t id = token_ids[t] < 0 ? 0 : token_ids[t];"),
+    "hash drop mode lets one token too many in": ("if (held[e] >= cap) {", "if (held[e] > cap) {"),
     "group limit keeps one group too many": ("for (int i = 0; i < L->topk_group; ++i) kept[gid[i]] = 1;",
                                              "for (int i = 0; i <= L->topk_group && i < G; ++i) kept[gid[i]] = 1;"),
     "permutation in descending token order": ("for (int e = 0; e < E; ++e) fill[e] = offsets[e];\n  for (int64_t t = 0; t < T; ++t) {",
@@ -67,6 +83,11 @@ PINS = [
     lambda: S.test_drop_mode_is_the_unlimited_top_k_minus_late_assignments(8, 1, 1, 2, 0.75, "softmax"),
     lambda: S.test_selection_matches_exhaustive_enumeration(16, 4, 2, 3, "sigmoid"),
     P.test_hand_example,
+    V.test_sqrtsoftplus32_within_2ulp_of_double, V.test_sqrtsoftplus32_closed_forms,
+    V.test_without_bias_selection_is_the_top_k_of_the_logits, V.test_gates_closed_form,
+    V.test_bias_changes_selection_but_not_gates, V.test_hash_routing_hand_example,
+    V.test_hash_routing_follows_the_table_whatever_the_logits,
+    V.test_hash_routing_drop_mode_keeps_the_first_c_assignments,
     B.test_loads_at_the_mean_keep_their_bias, B.test_random_loads_against_library_entropy_and_float32_steps,
     F.test_swiglu_closed_form_with_selection_matrices, F.test_single_expert_layer_is_a_dense_swiglu_ffn,
     F.test_identical_experts_factor_out, F.test_empty_slots_are_skipped_and_bf16_inputs_are_exact,

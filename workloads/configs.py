@@ -1,9 +1,10 @@
-"""Layer shapes: the five workloads plus reduced shapes for full-oracle tests."""
+"""Layer shapes: the workloads plus reduced shapes for full-oracle tests."""
 from dataclasses import dataclass, replace
 from typing import Optional
 
 SOFTMAX = "softmax"
 SIGMOID = "sigmoid"
+SQRTSOFTPLUS = "sqrtsoftplus"
 
 
 @dataclass(frozen=True)
@@ -17,7 +18,7 @@ class LayerShape:
     I: int                      # expert intermediate size (routed and shared)
     G: int = 1                  # expert groups
     topk_group: int = 1         # groups kept per token
-    scoring: str = SOFTMAX      # "softmax" | "sigmoid"
+    scoring: str = SOFTMAX      # "softmax" | "sigmoid" | "sqrtsoftplus"
     renorm: bool = True         # renormalise the selected gates
     scale: float = 1.0          # routed scaling factor applied to the gates
     capacity_factor: float = 0.0  # <= 0: unlimited
@@ -25,6 +26,7 @@ class LayerShape:
     dtype: str = "bf16"         # "bf16" | "f32" for x and every weight
     sel_bias: Optional[float] = None   # selection bias ~ U(-a, a) when set
     zipf_s: Optional[float] = None     # Zipf exponent of the per-expert logit offset
+    hash_vocab: int = 0         # > 0: hash routing through a [hash_vocab, k] token-id table
     seed: int = 0
 
     def with_(self, **kw) -> "LayerShape":
@@ -60,6 +62,17 @@ CONFIGS = {
                                      I=2048, G=8, topk_group=4, scoring=SIGMOID, renorm=True,
                                      scale=2.5, sel_bias=0.05, zipf_s=1.1, capacity_factor=1.25,
                                      seed=505),
+    # DeepSeek-V4-Flash-shaped layer, prefill size: sqrt(softplus) scores with
+    # the selection bias, no group limit.  The page gives H, E, S and k; the
+    # expert width is not printed, 2048 (V3's) makes the experts of its 43
+    # layers 278B of the 284B total it states.
+    "deepseek_v4_flash": LayerShape("deepseek_v4_flash", T=16384, H=4096, E=256, S=1, k=6, I=2048,
+                                    scoring=SQRTSOFTPLUS, renorm=True, scale=1.0, sel_bias=0.05, seed=606),
+    # The same layer with hash routing (V4's first layers): a fixed table over
+    # the 129,280-entry vocabulary chooses, the router only weights.
+    "deepseek_v4_flash_hash": LayerShape("deepseek_v4_flash_hash", T=16384, H=4096, E=256, S=1, k=6, I=2048,
+                                         scoring=SQRTSOFTPLUS, renorm=True, scale=1.0, hash_vocab=129280,
+                                         seed=707),
 }
 
 # Reduced shapes with the same routing structure, small enough for the full
@@ -71,6 +84,9 @@ TEST_SHAPES = {
     "v2_small": CONFIGS["deepseek_v2"].with_(name="v2_small", T=301, H=512, I=384),
     "v3_small": CONFIGS["deepseek_v3_prefill"].with_(name="v3_small", T=517, H=512, I=256),
     "v3_decode_small": CONFIGS["deepseek_v3_decode"].with_(name="v3_decode_small", H=512, I=256),
+    "v4_small": CONFIGS["deepseek_v4_flash"].with_(name="v4_small", T=517, H=512, I=256),
+    "v4_hash_small": CONFIGS["deepseek_v4_flash_hash"].with_(name="v4_hash_small", T=389, H=512, I=256,
+                                                             hash_vocab=3000),
 }
 
 

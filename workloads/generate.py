@@ -2,7 +2,9 @@
 
 Distributions: x ~ N(0, 1); every weight ~ N(0, 1/fan_in) (router and gate/up:
 fan_in = H; down: fan_in = I); optional selection bias ~ U(-a, a) in fp32;
-optional Zipf(s) per-expert logit offset.  bf16 tensors are produced by
+optional Zipf(s) per-expert logit offset; for hash routing, token ids with
+Zipf(1) frequencies over the vocabulary and a table of k distinct uniformly
+drawn experts per id.  bf16 tensors are produced by
 rounding fp32 draws to nearest-even (torch's conversion).
 
 The random stream of each tensor is a torch Philox/CPU generator seeded from
@@ -16,7 +18,7 @@ import math
 import numpy as np
 import torch
 
-_TENSORS = ("x", "w_router", "sel_bias", "zipf_perm", "w_gate", "w_up", "w_down")
+_TENSORS = ("x", "w_router", "sel_bias", "zipf_perm", "w_gate", "w_up", "w_down", "token_ids", "tid2eid")
 
 
 def _seed(base: int, name: str) -> int:
@@ -50,10 +52,33 @@ def zipf_logit_offsets(E: int, s: float, seed: int) -> np.ndarray:
     return (logp - logp.mean()).astype(np.float32)
 
 
+def hash_table(vocab: int, E: int, k: int, seed: int) -> np.ndarray:
+    """[vocab, k] int32 table of k distinct experts per row, uniform over the
+    k-subsets of E in random order (rows with a repeat are drawn again)."""
+    rng = np.random.Generator(np.random.PCG64(_seed(seed, "tid2eid")))
+    tab = rng.integers(0, E, (vocab, k), dtype=np.int64)
+    while True:
+        srt = np.sort(tab, axis=1)
+        bad = np.nonzero((srt[:, 1:] == srt[:, :-1]).any(axis=1))[0] if k > 1 else np.zeros(0, np.int64)
+        if bad.size == 0:
+            return tab.astype(np.int32)
+        tab[bad] = rng.integers(0, E, (bad.size, k), dtype=np.int64)
+
+
+def zipf_token_ids(T: int, vocab: int, seed: int, s: float = 1.0) -> np.ndarray:
+    """[T] int32 token ids with Zipf(s) frequencies over the vocabulary (the
+    rank-frequency law of text), ranks assigned to ids by a seeded permutation."""
+    rng = np.random.Generator(np.random.PCG64(_seed(seed, "token_ids")))
+    p = np.arange(1, vocab + 1, dtype=np.float64) ** -s
+    ranks = rng.choice(vocab, size=T, p=p / p.sum())
+    return rng.permutation(vocab)[ranks].astype(np.int32)
+
+
 def make_inputs(cfg, device="cpu", seed=None, T=None):
     """Return a dict of tensors on `device`:
     x [T,H], w_router [E,H], w_gate/w_up [E+S,I,H], w_down [E+S,H,I] in the
-    layer dtype; sel_bias [E] fp32 or None; logit_bias [E] fp32 or None."""
+    layer dtype; sel_bias [E] fp32 or None; logit_bias [E] fp32 or None;
+    with hash routing token_ids [T] and tid2eid [vocab,k] int32, else None."""
     base = cfg.seed if seed is None else seed
     T = cfg.T if T is None else T
     dt = _dtype(cfg)
@@ -71,6 +96,12 @@ def make_inputs(cfg, device="cpu", seed=None, T=None):
         out["logit_bias"] = torch.from_numpy(zipf_logit_offsets(E, cfg.zipf_s, base)).to(device)
     else:
         out["logit_bias"] = None
+    vocab = getattr(cfg, "hash_vocab", 0)
+    if vocab > 0:
+        out["token_ids"] = torch.from_numpy(zipf_token_ids(T, vocab, base)).to(device)
+        out["tid2eid"] = torch.from_numpy(hash_table(vocab, E, cfg.k, base)).to(device)
+    else:
+        out["token_ids"] = out["tid2eid"] = None
     for name, shape, std in (("w_gate", (I, H), 1.0 / math.sqrt(H)),
                              ("w_up", (I, H), 1.0 / math.sqrt(H)),
                              ("w_down", (H, I), 1.0 / math.sqrt(I))):
