@@ -1,8 +1,8 @@
 """Benchmark of the MoE layer on one MI355X.
 
-One step = one moe_forward call (router, capacity when configured, permute,
-gate/up+SwiGLU GEMM, down GEMM, combine) over one batch of seeded synthetic
-inputs already resident in HBM.  Default workload: the DeepSeek-V3-shaped
+One step = one moe_forward call (moe_forward_hash for hash-routed workloads):
+router, capacity when configured, permute, gate/up+SwiGLU GEMM, down GEMM,
+combine, over one batch of seeded synthetic inputs already resident in HBM.  Default workload: the DeepSeek-V3-shaped
 prefill layer (16384 tokens, hidden 7168, 256 routed + 1 shared experts,
 top-8 of 8 groups / 4 kept, intermediate 2048, bf16).
 
@@ -26,7 +26,6 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec at DeepSeek-V3 shape; % bf16 MFMA peak / % HBM BW"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_swiglu_deepseek_v3_prefill_traffic.md")
 GEMM_SRC = os.path.join(ROOT, "routing_expert_ffn_amd", "csrc", "gemm.hip")
 
 
@@ -39,12 +38,14 @@ def gemm_source_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed counter summary, or
-    None when the summary is missing or was taken on another kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary of
+    this workload, or None when it is missing or was taken on another kernel
+    source."""
+    path = os.path.join(ROOT, "profiles", "gateup_swiglu_%s_traffic.md" % workload)
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     sha = re.search(r"gemm_source_sha:\s*([0-9a-f]+)", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not sha or not val or sha.group(1) != gemm_source_sha():
@@ -67,6 +68,7 @@ def cpu_baseline(shape, inp, target_s):
     sb = to_oracle(inp["sel_bias"])
     lb = to_oracle(inp["logit_bias"])
     wg, wu, wd = to_oracle(inp["w_gate"]), to_oracle(inp["w_up"]), to_oracle(inp["w_down"])
+    ids, tab = to_oracle(inp["token_ids"]), to_oracle(inp["tid2eid"])
     torch.cuda.synchronize()
     rng = np.random.default_rng(77)
     order = rng.permutation(shape.T)
@@ -74,7 +76,10 @@ def cpu_baseline(shape, inp, target_s):
     def run(tokens):
         t0 = time.perf_counter()
         logits = oracle.router_logits(shape, x[tokens], wr, lb)
-        idx, w, _, _ = oracle.select(shape, logits, sb)
+        if tab is not None:
+            idx, w, _ = oracle.hash_select(shape, logits, ids[tokens], tab)
+        else:
+            idx, w, _, _ = oracle.select(shape, logits, sb)
         oracle.forward_tokens(shape, np.arange(len(tokens)), x[tokens], idx, w, lambda e: (wg[e], wu[e], wd[e]))
         return time.perf_counter() - t0
 
@@ -136,9 +141,14 @@ def main():
         log("calibration: 3 device copies of 1 GiB")
 
     def step():
-        moe.forward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
-                    logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], out=out, topk_idx=idx,
-                    expert_counts=counts, ws=ws)
+        if inp["tid2eid"] is not None:
+            moe.forward_hash(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                             inp["token_ids"], inp["tid2eid"], logit_bias=inp["logit_bias"], out=out, topk_idx=idx,
+                             expert_counts=counts, ws=ws)
+        else:
+            moe.forward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                        logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], out=out, topk_idx=idx,
+                        expert_counts=counts, ws=ws)
 
     for _ in range(args.warmup):
         step()
@@ -186,9 +196,9 @@ def main():
         "config": {"workload": shape.name, "tokens": T, "hidden": shape.H, "routed_experts": shape.E,
                    "shared_experts": shape.S, "top_k": shape.k, "groups": shape.G, "groups_kept": shape.topk_group,
                    "intermediate": shape.I, "scoring": shape.scoring, "capacity_factor": shape.capacity_factor,
-                   "out_dtype": "bf16"},
+                   "routing": "hash" if shape.hash_vocab else "learned", "out_dtype": "bf16"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(shape.name),
                      "kernel": "gateup_swiglu", "flops_per_launch": gateup_flops, "ms_per_launch": gu_ms},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
         "layer_mfma_frac": layer_flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

@@ -6,6 +6,8 @@
  *   router logits   l = x W_r^T (+ logit_bias)            "MoE架构揭秘：大模型参数激活率与专家路由机制解析", 3.1
  *   scoring         softmax over E logits                 same section
  *                   or sigmoid + selection-only bias      "15. DeepSeek：MLA、MoE 与 MTP", "V3 的 MoE：256 个专家怎样选 8 个"
+ *                   or sqrt(softplus) + selection bias    same page, "V4：放弃潜向量，改用压缩注意力" (FFN paragraph)
+ *   hash routing    experts fixed by a token-id table     same V4 paragraph (moe_route_hash, moe_forward_hash)
  *   group limit     groups of E/G experts scored by the sum of their two best
  *                   biased scores, topk_group groups kept  same DeepSeek section
  *   top-k + gates   renormalised softmax ("GPT-4 Has 1.8 Trillion Parameters.
@@ -62,7 +64,7 @@ typedef enum {
   MOE_ERR_HIP = -4          /* a HIP runtime call failed                    */
 } moe_status;
 
-typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SQRTSOFTPLUS = 2 } moe_scoring;
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Layer description: the fields the DeepSeek page reads from a checkpoint's
@@ -97,19 +99,27 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
  *   x            [T,H] input dtype (unused when logits_in is given)
  *   w_router     [E,H] input dtype (unused when logits_in is given)
  *   logit_bias   [E] fp32 added to every logit, or NULL
- *   sel_bias     [E] fp32 selection-only bias (sigmoid scoring), or NULL
+ *   sel_bias     [E] fp32 selection-only bias (sigmoid and sqrt(softplus)
+ *                scoring), or NULL
  *   logits_in    [T,E] fp32 logits to route instead of computing them, or NULL
  *   logits_out   [T,E] fp32 computed logits (bias included), or NULL
  *   topk_idx     [T,k] int32 out: chosen experts in rank order, -1 = empty slot
  *   topk_w       [T,k] fp32 out: gates (0 for an empty slot)
  *   expert_counts[E] int32 out: tokens per expert, or NULL
  * Selection score: softmax scoring ranks the fp32 logits; sigmoid scoring
- * ranks c_e = fl32(sigmoid32(l_e) + sel_bias_e), where sigmoid32 clamps l to
+ * ranks c_e = fl32(sigmoid32(l_e) + sel_bias_e) and sqrt(softplus) scoring
+ * c_e = fl32(sqrtsoftplus32(l_e) + sel_bias_e), where sigmoid32 clamps l to
  * [-80,80] and evaluates 1/(1+e) (l >= 0, e = exp32(-l)) or e/(1+e) (l < 0,
  * e = exp32(l)); exp32(z) = ldexp(p(r), n), n = rint(fl32(z*0x1.715476p+0)),
  * r = fma(-n, 0x1.7f7d1cp-20, fma(-n, 0x1.62e4p-1, z)), p = Horner with fma of
  * the fp32 coefficients {1, 1, 0x1p-1, 0x1.555556p-3, 0x1.555556p-5,
- * 0x1.111112p-7, 0x1.6c16c2p-10, 0x1.a01a02p-13}.  Group score = fl32(best +
+ * 0x1.111112p-7, 0x1.6c16c2p-10, 0x1.a01a02p-13}; sqrtsoftplus32(l) =
+ * sqrt(fl32(max(l,0) + log1p32(exp32(-min(|l|,80))))) with the correctly
+ * rounded square root, log1p32(u) = fl32(fl32(z+z) * q), z = u/fl32(2+u),
+ * q = Horner with fma in w = fl32(z*z) of the fp32 coefficients {1,
+ * 0x1.555556p-2, 0x1.99999ap-3, 0x1.24924ap-3, 0x1.c71c72p-4, 0x1.745d18p-4,
+ * 0x1.3b13b2p-4, 0x1.111112p-4} (1/(2j+1)).  Gates of sigmoid and
+ * sqrt(softplus) scoring use the unbiased score.  Group score = fl32(best +
  * second best) of a group's c.  Ties rank the lower index first.
  * Capacity: tokens in index order each take their best-ranked allowed experts
  * with fewer than C tokens so far; C = ceil(((cf*T)*k)/E) in double.  With
@@ -124,6 +134,26 @@ moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void
                      const float* logit_bias, const float* sel_bias, const float* logits_in,
                      float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Hash routing ("15. DeepSeek：MLA、MoE 与 MTP", section "V4：放弃潜向量，改用压缩注意力",
+ * FFN paragraph: in its first layers a fixed table keyed by the token id picks
+ * the experts and the router only weights them).  Arguments as moe_route,
+ * plus
+ *   token_ids    [T] int32 device: id of every token
+ *   tid2eid      [vocab,k] int32 device: experts of every id, in slot order
+ *                (NULL allowed only when vocab == 0)
+ *   vocab        rows of tid2eid, >= 0
+ * Slot j of token t takes e = tid2eid[token_ids[t], j]; a token id outside
+ * [0, vocab) takes no expert; an entry outside [0, E) or equal to an earlier
+ * entry of its row leaves its slot empty (-1, gate 0).  The gates are those
+ * of cfg's scoring over the chosen experts (the logits are still computed;
+ * sel_bias does not apply).  A capacity limit needs drop_tokens = 1 (there
+ * is no next-best expert to re-route to; MOE_ERR_INVALID_ARG otherwise).
+ * Workspace: required for bf16 layers that compute their logits. */
+moe_status moe_route_hash(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                          const float* logit_bias, const float* logits_in, float* logits_out, const int32_t* token_ids,
+                          const int32_t* tid2eid, int64_t vocab, int32_t* topk_idx, float* topk_w,
+                          int32_t* expert_counts, void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch: expert histogram and stable permutation of (token, slot) pairs.
  *   topk_idx       [T,k] int32, each row distinct experts in [0,E) or -1
@@ -163,6 +193,14 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
                        const float* logit_bias, const float* sel_bias, const void* w_gate, const void* w_up,
                        const void* w_down, void* out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
                        float* logits_out, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward with hash routing (moe_route_hash's selection): token_ids,
+ * tid2eid and vocab as there, every other argument as moe_forward. */
+moe_status moe_forward_hash(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                            const float* logit_bias, const int32_t* token_ids, const int32_t* tid2eid, int64_t vocab,
+                            const void* w_gate, const void* w_up, const void* w_down, void* out, int32_t* topk_idx,
+                            float* topk_w, int32_t* expert_counts, float* logits_out, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* One step of auxiliary-loss-free load balancing ("15. DeepSeek：MLA、MoE 与
  * MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the bias paragraph) and the

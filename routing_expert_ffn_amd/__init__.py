@@ -15,13 +15,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
+SCORING = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID, "sqrtsoftplus": MOE_SCORE_SQRTSOFTPLUS}
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
           -4: "MOE_ERR_HIP"}
 
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_balance_update", "moe_last_error", "moe_version", "moe_timing_enable", "moe_timing_read",
-           "moe_kernel_name")
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn", "moe_combine",
+           "moe_forward", "moe_forward_hash", "moe_balance_update", "moe_last_error", "moe_version",
+           "moe_timing_enable", "moe_timing_read", "moe_kernel_name")
 
 
 class MoeError(RuntimeError):
@@ -46,7 +47,7 @@ def make_config(shape, out_dtype=None):
     dt = MOE_F32 if shape.dtype == "f32" else MOE_BF16
     od = dt if out_dtype is None else (MOE_F32 if out_dtype in ("f32", torch.float32, MOE_F32) else MOE_BF16)
     return moe_config(shape.H, shape.E, shape.S, shape.k, shape.G, shape.topk_group, shape.I,
-                      MOE_SCORE_SIGMOID if shape.scoring == "sigmoid" else MOE_SCORE_SOFTMAX,
+                      SCORING[shape.scoring],
                       1 if shape.renorm else 0, float(shape.scale), float(shape.capacity_factor), dt, od,
                       1 if getattr(shape, "drop_tokens", False) else 0)
 
@@ -65,8 +66,9 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         C = ctypes.POINTER(moe_config)
-        for name in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-                     "moe_forward", "moe_balance_update", "moe_timing_enable", "moe_timing_read"):
+        for name in ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn",
+                     "moe_combine", "moe_forward", "moe_forward_hash", "moe_balance_update", "moe_timing_enable",
+                     "moe_timing_read"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [C, I64, ctypes.POINTER(SZ)]
         L.moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -75,6 +77,8 @@ def lib():
         L.moe_combine.argtypes = [C, I64, P, P, P, P, P]
         L.moe_balance_update.argtypes = [C, P, P, ctypes.c_float, P, P, P]
         L.moe_forward.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_route_hash.argtypes = [C, I64, P, P, P, P, P, P, P, I64, P, P, P, P, SZ, P]
+        L.moe_forward_hash.argtypes = [C, I64, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_version.restype = ctypes.c_char_p
@@ -133,6 +137,24 @@ def route(cfg, T, x=None, w_router=None, logit_bias=None, sel_bias=None, logits_
     _check(lib().moe_route(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(sel_bias), _p(logits_in),
                            _p(logits_out), _p(topk_idx), _p(topk_w), _p(expert_counts), _p(ws),
                            0 if ws is None else ws.numel(), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def route_hash(cfg, T, token_ids, tid2eid, x=None, w_router=None, logit_bias=None, logits_in=None,
+               logits_out=None, topk_idx=None, topk_w=None, expert_counts=None, ws=None, stream=None):
+    """Hash routing: token_ids [T] int32, tid2eid [vocab,k] int32 (device).
+    -> (topk_idx [T,k] int32, topk_w [T,k] fp32)"""
+    dev = _dev(x if x is not None else logits_in)
+    k = cfg.top_k
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(cfg, T, dev)
+    _check(lib().moe_route_hash(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(logits_in),
+                                _p(logits_out), _p(token_ids), _p(tid2eid), int(tid2eid.shape[0]), _p(topk_idx),
+                                _p(topk_w), _p(expert_counts), _p(ws), ws.numel(), _stream(stream)))
     return topk_idx, topk_w
 
 
@@ -199,6 +221,22 @@ def forward(cfg, x, w_router, w_gate, w_up, w_down, logit_bias=None, sel_bias=No
     _check(lib().moe_forward(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(sel_bias), _p(w_gate),
                              _p(w_up), _p(w_down), _p(out), _p(topk_idx), _p(topk_w), _p(expert_counts),
                              _p(logits_out), _p(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def forward_hash(cfg, x, w_router, w_gate, w_up, w_down, token_ids, tid2eid, logit_bias=None, out=None,
+                 topk_idx=None, topk_w=None, expert_counts=None, logits_out=None, ws=None, stream=None):
+    """The whole layer with hash routing; -> out [T,H] in cfg.out_dtype."""
+    T = x.shape[0]
+    if out is None:
+        dt = torch.float32 if cfg.out_dtype == MOE_F32 else torch.bfloat16
+        out = torch.empty((T, cfg.hidden_size), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(cfg, T, x.device)
+    _check(lib().moe_forward_hash(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(token_ids),
+                                  _p(tid2eid), int(tid2eid.shape[0]), _p(w_gate), _p(w_up), _p(w_down), _p(out),
+                                  _p(topk_idx), _p(topk_w), _p(expert_counts), _p(logits_out), _p(ws), ws.numel(),
+                                  _stream(stream)))
     return out
 
 

@@ -77,8 +77,8 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
   if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32 or MOE_BF16");
   if (d.out_dtype != MOE_F32 && d.out_dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_F32 or MOE_BF16");
-  if (d.scoring != MOE_SCORE_SOFTMAX && d.scoring != MOE_SCORE_SIGMOID)
-    return fail(MOE_ERR_INVALID_ARG, "scoring must be MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID");
+  if (d.scoring != MOE_SCORE_SOFTMAX && d.scoring != MOE_SCORE_SIGMOID && d.scoring != MOE_SCORE_SQRTSOFTPLUS)
+    return fail(MOE_ERR_INVALID_ARG, "scoring must be MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID or MOE_SCORE_SQRTSOFTPLUS");
   if (d.H <= 0 || d.I <= 0) return fail(MOE_ERR_INVALID_ARG, "hidden_size and moe_intermediate_size must be > 0");
   if (d.E < 1) return fail(MOE_ERR_INVALID_ARG, "n_routed_experts must be >= 1");
   if (d.E > 512) return fail(MOE_ERR_UNSUPPORTED, "n_routed_experts > 512 is not supported");
@@ -225,10 +225,34 @@ hipError_t run_router(const Dims& d, RouterArgs a, const void* x, const void* w_
   return timed(K_ROUTE_SELECT, s, [&] { return launch_route_select(a, s); });
 }
 
+// Hash routing inputs (null table: learned routing).
+struct HashTable {
+  const int32_t* token_ids = nullptr;
+  const int32_t* tid2eid = nullptr;
+  int64_t vocab = 0;
+};
+
+moe_status check_hash(const Dims& d, const int32_t* token_ids, const int32_t* tid2eid, int64_t vocab) {
+  if (vocab < 0) return fail(MOE_ERR_INVALID_ARG, "vocab must be >= 0");
+  if (vocab > INT64_MAX / 32) return fail(MOE_ERR_INVALID_ARG, "vocab too large");
+  if (d.T > 0 && !token_ids) return fail(MOE_ERR_INVALID_ARG, "token_ids is required");
+  if (d.T > 0 && vocab > 0 && !tid2eid) return fail(MOE_ERR_INVALID_ARG, "tid2eid is required when vocab > 0");
+  if (d.capacity > 0 && !d.drop)
+    return fail(MOE_ERR_INVALID_ARG, "hash routing has no next-best expert: a capacity needs drop_tokens = 1");
+  return MOE_OK;
+}
+
 moe_status do_route(const Dims& d, const void* x, const void* w_router, const float* logit_bias,
                     const float* sel_bias, const float* logits_in, float* logits_out, int32_t* topk_idx,
-                    float* topk_w, int32_t* counts, void* ws, const Layout& L, hipStream_t s) {
+                    float* topk_w, int32_t* counts, void* ws, const Layout& L, hipStream_t s,
+                    const HashTable* hash = nullptr) {
   RouterArgs a{};
+  if (hash) {
+    a.hash = 1;
+    a.token_ids = hash->token_ids;
+    a.tid2eid = hash->tid2eid;
+    a.vocab = hash->vocab;
+  }
   a.p = route_params(d);
   a.x = x;
   a.w_router = w_router;
@@ -401,6 +425,49 @@ moe_status do_combine(const Dims& d, const void* y_routed, bool routed_bf16, con
   return MOE_OK;
 }
 
+// The whole layer (learned routing, or hash routing when `hash` is set).
+moe_status forward_impl(const Dims& d, const void* x, const void* w_router, const float* logit_bias,
+                        const float* sel_bias, const void* w_gate, const void* w_up, const void* w_down, void* out,
+                        int32_t* topk_idx, float* topk_w, int32_t* expert_counts, float* logits_out, void* ws,
+                        size_t ws_bytes, hipStream_t s, const HashTable* hash) {
+  moe_status st;
+  if (d.T == 0) return MOE_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(out))
+    return fail(MOE_ERR_INVALID_ARG, "x, weights and out must be 16-byte aligned");
+  Layout L{};
+  st = check_ws(d, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* w = topk_w ? topk_w : at<float>(ws, L.w);
+  int32_t* counts = expert_counts ? expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  int32_t* slot_row = at<int32_t>(ws, L.slot_row);
+  void* y = at<void>(ws, L.y);
+  st = do_route(d, x, w_router, logit_bias, sel_bias, nullptr, logits_out, idx, w, nullptr, ws, L, s, hash);
+  if (st != MOE_OK) return st;
+  st = do_permute(d, idx, counts, offsets, row_token, slot_row, ws, L, s);
+  if (st != MOE_OK) return st;
+  if (d.dtype == MOE_BF16 && d.S >= 1) {
+    // routed expert rows in bf16, shared expert rows in fp32, in the
+    // expert-row region: with a shared expert, whose unweighted fp32 row
+    // carries much of each output, the bf16 rounding of the gate-weighted
+    // routed rows stays small against the output (measured: 0.0074 ->
+    // 0.0090 of RMS at the DeepSeek-V3 prefill shape); without one, every
+    // output is a sum of rounded rows and all rows stay fp32
+    void* y16 = y;
+    float* y32 = reinterpret_cast<float*>(static_cast<char*>(y) + (size_t)d.T * d.k * d.H * 2);
+    st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y32, ws, L, s, y16);
+    if (st != MOE_OK) return st;
+    return do_combine(d, y16, true, y32, slot_row, w, out, s);
+  }
+  st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y, ws, L, s);
+  if (st != MOE_OK) return st;
+  return do_combine(d, y, false, static_cast<const float*>(y) + (int64_t)d.T * d.k * d.H, slot_row, w, out, s);
+}
+
 }  // namespace
 
 // ---- kernel names --------------------------------------------------------------
@@ -501,44 +568,49 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
                        int32_t* topk_idx, float* topk_w, int32_t* expert_counts, float* logits_out, void* ws,
                        size_t ws_bytes, void* stream) {
   Dims d;
+  const moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  return forward_impl(d, x, w_router, logit_bias, sel_bias, w_gate, w_up, w_down, out, topk_idx, topk_w,
+                      expert_counts, logits_out, ws, ws_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+moe_status moe_route_hash(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                          const float* logit_bias, const float* logits_in, float* logits_out, const int32_t* token_ids,
+                          const int32_t* tid2eid, int64_t vocab, int32_t* topk_idx, float* topk_w,
+                          int32_t* expert_counts, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
   moe_status st = check_config(cfg, T, d);
   if (st != MOE_OK) return st;
+  st = check_hash(d, token_ids, tid2eid, vocab);
+  if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
-  if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
-      !aligned16(out))
-    return fail(MOE_ERR_INVALID_ARG, "x, weights and out must be 16-byte aligned");
+  if (!logits_in && (!x || !w_router)) return fail(MOE_ERR_INVALID_ARG, "x and w_router are required without logits_in");
+  if (!logits_in && (!aligned16(x) || !aligned16(w_router)))
+    return fail(MOE_ERR_INVALID_ARG, "x and w_router must be 16-byte aligned");
+  if (!topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "topk_idx and topk_w are required");
   Layout L{};
-  st = check_ws(d, ws, ws_bytes, L);
-  if (st != MOE_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
-  float* w = topk_w ? topk_w : at<float>(ws, L.w);
-  int32_t* counts = expert_counts ? expert_counts : at<int32_t>(ws, L.counts);
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* row_token = at<int32_t>(ws, L.row_token);
-  int32_t* slot_row = at<int32_t>(ws, L.slot_row);
-  void* y = at<void>(ws, L.y);
-  st = do_route(d, x, w_router, logit_bias, sel_bias, nullptr, logits_out, idx, w, nullptr, ws, L, s);
-  if (st != MOE_OK) return st;
-  st = do_permute(d, idx, counts, offsets, row_token, slot_row, ws, L, s);
-  if (st != MOE_OK) return st;
-  if (d.dtype == MOE_BF16 && d.S >= 1) {
-    // routed expert rows in bf16, shared expert rows in fp32, in the
-    // expert-row region: with a shared expert, whose unweighted fp32 row
-    // carries much of each output, the bf16 rounding of the gate-weighted
-    // routed rows stays small against the output (measured: 0.0074 ->
-    // 0.0090 of RMS at the DeepSeek-V3 prefill shape); without one, every
-    // output is a sum of rounded rows and all rows stay fp32
-    void* y16 = y;
-    float* y32 = reinterpret_cast<float*>(static_cast<char*>(y) + (size_t)d.T * d.k * d.H * 2);
-    st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y32, ws, L, s, y16);
+  if (!logits_in && d.dtype == MOE_BF16) {
+    st = check_ws(d, ws, ws_bytes, L);
     if (st != MOE_OK) return st;
-    return do_combine(d, y16, true, y32, slot_row, w, out, s);
   }
-  st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y, ws, L, s);
+  const HashTable h{token_ids, tid2eid, vocab};
+  return do_route(d, x, w_router, logit_bias, nullptr, logits_in, logits_out, topk_idx, topk_w, expert_counts, ws, L,
+                  static_cast<hipStream_t>(stream), &h);
+}
+
+moe_status moe_forward_hash(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                            const float* logit_bias, const int32_t* token_ids, const int32_t* tid2eid, int64_t vocab,
+                            const void* w_gate, const void* w_up, const void* w_down, void* out, int32_t* topk_idx,
+                            float* topk_w, int32_t* expert_counts, float* logits_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  Dims d;
+  moe_status st = check_config(cfg, T, d);
   if (st != MOE_OK) return st;
-  return do_combine(d, y, false, static_cast<const float*>(y) + (int64_t)d.T * d.k * d.H, slot_row, w, out, s);
+  st = check_hash(d, token_ids, tid2eid, vocab);
+  if (st != MOE_OK) return st;
+  const HashTable h{token_ids, tid2eid, vocab};
+  return forward_impl(d, x, w_router, logit_bias, nullptr, w_gate, w_up, w_down, out, topk_idx, topk_w,
+                      expert_counts, logits_out, ws, ws_bytes, static_cast<hipStream_t>(stream), &h);
 }
 
 moe_status moe_balance_update(const moe_config* cfg, const int32_t* expert_counts, float* sel_bias, float gamma,

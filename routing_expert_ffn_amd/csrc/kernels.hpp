@@ -7,7 +7,7 @@
 struct RouteParams {
   int T, H, E, k;
   int G, gsz, topk_group;
-  int scoring;   // 0 softmax, 1 sigmoid
+  int scoring;   // 0 softmax, 1 sigmoid, 2 sqrt(softplus)
   int renorm;
   float scale;
   int capacity;  // <= 0: unlimited
@@ -28,6 +28,10 @@ struct RouterArgs {
   float* topk_w;            // [T,k]
   int32_t* counts;          // [E] atomically incremented, or null
   int32_t* cand;            // capacity mode: [T,n_allowed] experts in rank order
+  int hash;                 // 1: hash routing through token_ids and tid2eid
+  const int32_t* token_ids; //   [T] token ids
+  const int32_t* tid2eid;   //   [vocab,k] expert table (unread when vocab == 0)
+  int64_t vocab;
 };
 
 // Router GEMM (bf16): logits of 64-token tiles over K slices of sps steps of

@@ -7,14 +7,18 @@
 // It Uses 2% of Them Per Token", section 2.2):
 //   l = x W_r^T (+ logit_bias)
 //   softmax scoring: rank the fp32 logits; sigmoid scoring: rank
-//   c = fl32(sigmoid32(l) + sel_bias)
+//   c = fl32(sigmoid32(l) + sel_bias); sqrt(softplus) scoring (same page,
+//   section "V4：放弃潜向量，改用压缩注意力"): c = fl32(sqrtsoftplus32(l) + sel_bias)
+//   hash routing (same V4 section): experts from a fixed token-id table, the
+//   logits only give the gates
 //   G > 1: group score = fl32(best + second best c of the group), keep the
 //   topk_group best groups, rank only their experts
 //   top-k in rank order (ties: lower index), gates per moe.h
 //   capacity: tokens in order take their best-ranked allowed experts with room.
 //
 // This translation unit is compiled without floating-point contraction so the
-// fp32 sigmoid below is exactly the documented sequence of roundings.
+// fp32 sigmoid and sqrt(softplus) below are exactly the documented sequences
+// of roundings.
 #include <algorithm>
 
 #include "common.hpp"
@@ -58,6 +62,40 @@ __device__ __forceinline__ float sigmoid32(float l) {
   return e / d;
 }
 
+// log(1 + u) for 0 < u <= 1: 2 atanh(z) with z = u / (2 + u) <= 1/3; the odd
+// series of atanh in w = z^2 through the w^7 term (coefficients 1/(2j+1)
+// rounded to fp32), Horner form with fused multiply-adds.
+__device__ __forceinline__ float log1p32_unit(float u) {
+  const float d = 2.0f + u;
+  const float z = u / d;
+  const float w = z * z;
+  float q = 0x1.111112p-4f;
+  q = __builtin_fmaf(q, w, 0x1.3b13b2p-4f);
+  q = __builtin_fmaf(q, w, 0x1.745d18p-4f);
+  q = __builtin_fmaf(q, w, 0x1.c71c72p-4f);
+  q = __builtin_fmaf(q, w, 0x1.24924ap-3f);
+  q = __builtin_fmaf(q, w, 0x1.99999ap-3f);
+  q = __builtin_fmaf(q, w, 0x1.555556p-2f);
+  q = __builtin_fmaf(q, w, 0x1p+0f);
+  const float z2 = z + z;
+  return z2 * q;
+}
+
+// Selection sqrt(softplus): softplus(l) = max(l, 0) + log(1 + e^-a) with
+// a = min(|l|, 80), then the correctly rounded fp32 square root.
+__device__ __forceinline__ float sqrtsoftplus32(float l) {
+  float a = __builtin_fabsf(l);
+  a = a > 80.0f ? 80.0f : a;
+  const float u = exp32_nonpos(-a);
+  const float sp = (l > 0.0f ? l : 0.0f) + log1p32_unit(u);
+  return __builtin_sqrtf(sp);
+}
+
+// Unbiased score of scoring 1 (sigmoid) or 2 (sqrt(softplus)).
+__device__ __forceinline__ float score32(int scoring, float l) {
+  return scoring == 2 ? sqrtsoftplus32(l) : sigmoid32(l);
+}
+
 __device__ __forceinline__ float ordered_to_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
@@ -73,8 +111,8 @@ __device__ __forceinline__ void token_scores(const RouteParams& p, const float* 
     if (e < p.E) {
       const float l = lrow[e];
       float c;
-      if (p.scoring == 1) {
-        const float s = sigmoid32(l);
+      if (p.scoring != 0) {
+        const float s = score32(p.scoring, l);
         const float b = sel_bias ? sel_bias[e] : 0.0f;
         c = s + b;
       } else {
@@ -128,8 +166,8 @@ template <int NJ>
 __device__ __forceinline__ float token_gate(const RouteParams& p, const float* lrow, int my_e, int lane) {
   const bool mine = lane < p.k && my_e >= 0;
   float g = 0.0f;
-  if (p.scoring == 1) {
-    const float s = mine ? sigmoid32(lrow[my_e]) : 0.0f;
+  if (p.scoring != 0) {
+    const float s = mine ? score32(p.scoring, lrow[my_e]) : 0.0f;
     if (p.renorm) {
       const float tot = wave_sum_f32(s);
       g = mine ? s / tot : 0.0f;
@@ -137,10 +175,9 @@ __device__ __forceinline__ float token_gate(const RouteParams& p, const float* l
       g = s;
     }
   } else if (p.renorm) {
-    // softmax renormalised over the selection = softmax of the chosen logits;
-    // the slot-0 expert has the largest chosen logit
+    // softmax renormalised over the selection = softmax of the chosen logits
     const float l = mine ? lrow[my_e] : 0.0f;
-    const float m0 = __shfl(l, 0);
+    const float m0 = wave_max_f32(mine ? l : -INFINITY);
     const float ex = mine ? expf(l - m0) : 0.0f;
     const float tot = wave_sum_f32(ex);
     g = mine ? ex / tot : 0.0f;
@@ -220,6 +257,26 @@ __device__ __forceinline__ void wave_bitonic_desc(uint64_t (&key)[NJ], int lane)
 template <int NJ>
 __device__ __forceinline__ void route_token(const RouterArgs& a, const float* lrow, int t, int lane) {
   const RouteParams& p = a.p;
+  if (a.hash) {
+    // hash routing: row token_ids[t] of the table chooses, the logits only
+    // weight; an entry out of [0, E) or repeating an earlier entry of the
+    // row, and every entry of an id outside the table, leave the slot empty
+    const int64_t id = a.token_ids[t];
+    const bool in_table = id >= 0 && id < a.vocab;
+    const int raw = (lane < p.k && in_table) ? a.tid2eid[id * p.k + lane] : -1;
+    int my_e = (raw >= 0 && raw < p.E) ? raw : -1;
+    for (int j = 0; j + 1 < p.k; ++j) {
+      const int rj = __shfl(raw, j);
+      if (j < lane && rj == my_e) my_e = -1;
+    }
+    const float g = token_gate<NJ>(p, lrow, my_e, lane);
+    if (lane < p.k) {
+      a.topk_idx[(int64_t)t * p.k + lane] = my_e;
+      a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
+      if (a.counts && my_e >= 0) atomicAdd(&a.counts[my_e], 1);
+    }
+    return;
+  }
   uint64_t key[NJ];
   token_scores<NJ>(p, lrow, a.sel_bias, lane, key);
   if (p.capacity > 0) {

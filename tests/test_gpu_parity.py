@@ -53,9 +53,15 @@ def run_layer(shape, inp, out_dtype):
         counts=torch.empty((shape.E,), dtype=torch.int32, device=dev),
         logits=torch.empty((T, shape.E), dtype=torch.float32, device=dev),
     )
-    g["out"] = moe.forward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
-                           logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], topk_idx=g["idx"], topk_w=g["w"],
-                           expert_counts=g["counts"], logits_out=g["logits"])
+    if inp.get("tid2eid") is not None:
+        g["out"] = moe.forward_hash(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                                    inp["token_ids"], inp["tid2eid"], logit_bias=inp["logit_bias"],
+                                    topk_idx=g["idx"], topk_w=g["w"], expert_counts=g["counts"],
+                                    logits_out=g["logits"])
+    else:
+        g["out"] = moe.forward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                               logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], topk_idx=g["idx"],
+                               topk_w=g["w"], expert_counts=g["counts"], logits_out=g["logits"])
     torch.cuda.synchronize()
     return {k: v.cpu() for k, v in g.items()}
 
@@ -74,8 +80,18 @@ def check_layer(shape, inp, g, tokens, out_dtype):
     lb = to_oracle(inp["logit_bias"])
     L = g["logits"].numpy()
     idx = g["idx"].numpy()
+    hashed = inp.get("tid2eid") is not None
+    if hashed:
+        ids, tab = to_oracle(inp["token_ids"]), to_oracle(inp["tid2eid"])
+
+        def select(logits, rows):
+            i, w, c = oracle.hash_select(shape, logits, ids[rows], tab)
+            return i, w, np.full(len(rows), np.inf), c
+    else:
+        def select(logits, rows):
+            return oracle.select(shape, logits, sb)
     # routing from identical logits: bit-exact for every token
-    oidx, ow, _, ocounts = oracle.select(shape, L, sb)
+    oidx, ow, _, ocounts = select(L, np.arange(L.shape[0]))
     assert np.array_equal(idx, oidx), "routing differs from the oracle on identical logits"
     assert np.array_equal(g["counts"].numpy(), ocounts)
     np.testing.assert_allclose(g["w"].numpy(), ow, rtol=1e-5, atol=1e-6)
@@ -86,7 +102,7 @@ def check_layer(shape, inp, g, tokens, out_dtype):
         ref_idx, ref_w = oidx[tokens], ow[tokens]
         keep = np.ones(len(tokens), bool)
     else:
-        ref_idx, ref_w, ref_margin, _ = oracle.select(shape, ol, sb)
+        ref_idx, ref_w, ref_margin, _ = select(ol, tokens)
         keep = ref_margin >= MARGIN
         assert np.array_equal(idx[tokens][keep], ref_idx[keep]), "indices differ from the oracle"
         ref_idx = np.where(keep[:, None], ref_idx, oidx[tokens])
@@ -122,7 +138,7 @@ def test_layer_reduced_shapes_all_tokens(name):
 # ---- whole layer at the workloads' full sizes, sampled tokens --------------------
 
 @pytest.mark.parametrize("name", ["deepseek_v3_decode", "deepseek_v3_prefill", "deepseek_v2", "mixtral_8x7b",
-                                  "tiny_mixtral_fp32"])
+                                  "tiny_mixtral_fp32", "deepseek_v4_flash", "deepseek_v4_flash_hash"])
 def test_layer_full_size_sampled_tokens(name):
     shape = CONFIGS[name]
     inp = make_inputs(shape, device="cuda")
@@ -242,6 +258,84 @@ def test_route_ties_and_sigmoid_near_ties_from_given_logits():
     oidx2, ow2, _, _ = oracle.select(sm, L, None)
     assert np.array_equal(idx2.cpu().numpy(), oidx2)
     np.testing.assert_allclose(w2.cpu().numpy(), ow2, rtol=1e-5, atol=1e-6)
+
+
+def test_sqrtsoftplus_near_ties_from_given_logits():
+    """sqrt(softplus) selection is bit-exact: logits one ulp apart, exact
+    ties, biases at the resolution of the scores, the clamp region and large
+    logits, with and without a group limit."""
+    base = TEST_SHAPES["v4_small"]
+    T, E = 320, base.E
+    rng = np.random.default_rng(6)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[:32] = -0.75
+    for r0, v in ((32, 0.3), (96, 2.5), (160, -1.7)):
+        b = np.float32(v)
+        L[r0:r0 + 64] = b + np.spacing(b) * rng.integers(0, 8, (64, E)).astype(np.float32)
+    L[224:256] = np.float32(95.0) * np.sign(rng.standard_normal((32, E))).astype(np.float32)
+    L[256:288] = rng.uniform(-200, 200, (32, E)).astype(np.float32)
+    sb = np.zeros(E, np.float32)
+    sb[::5] = np.float32(2.0 ** -23)
+    Lg = torch.from_numpy(L).cuda()
+    for shape in (base, base.with_(G=8, topk_group=4)):
+        cfg = moe.make_config(shape)
+        counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        idx, w = moe.route(cfg, T, logits_in=Lg, sel_bias=torch.from_numpy(sb).cuda(), expert_counts=counts)
+        torch.cuda.synchronize()
+        oidx, ow, _, oc = oracle.select(shape, L, sb)
+        assert np.array_equal(idx.cpu().numpy(), oidx)
+        assert np.array_equal(counts.cpu().numpy(), oc)
+        np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("scoring,renorm", [("sqrtsoftplus", True), ("sigmoid", True), ("softmax", True),
+                                            ("softmax", False)])
+def test_hash_routing_table_edge_cases(scoring, renorm):
+    """Repeated and out-of-range table entries, ids outside the table, and
+    gates of every scoring over the table's experts."""
+    shape = TEST_SHAPES["v4_hash_small"].with_(scoring=scoring, renorm=renorm, scale=1.7)
+    E, k, V, T = shape.E, shape.k, 97, 700
+    rng = np.random.default_rng(12)
+    tab = np.stack([rng.permutation(E)[:k] for _ in range(V)]).astype(np.int32)
+    tab[3, 2] = tab[3, 0]                 # repeated entries
+    tab[4, :] = tab[4, 1]
+    tab[5, 1], tab[5, 4] = -1, E          # out of range
+    tab[6, :] = 2 ** 30
+    ids = rng.integers(-3, V + 3, T).astype(np.int32)   # some outside the table
+    ids[:40] = np.arange(40) % 8
+    L = (rng.standard_normal((T, E)) * 3).astype(np.float32)
+    cfg = moe.make_config(shape)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    lo = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx, w = moe.route_hash(cfg, T, torch.from_numpy(ids).cuda(), torch.from_numpy(tab).cuda(),
+                            logits_in=torch.from_numpy(L).cuda(), logits_out=lo, expert_counts=counts)
+    torch.cuda.synchronize()
+    oidx, ow, oc = oracle.hash_select(shape, L, ids, tab)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    assert np.array_equal(lo.cpu().numpy(), L)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
+    assert (oidx < 0).any() and (oidx >= 0).any()
+
+
+@pytest.mark.parametrize("cf", [0.3, 1.25])
+def test_hash_routing_drop_capacity_and_empty_table(cf):
+    shape = TEST_SHAPES["v4_hash_small"].with_(capacity_factor=cf, drop_tokens=True)
+    inp = make_inputs(shape, device="cuda")
+    g = run_layer(shape, inp, "f32")
+    C = oracle.capacity(shape, shape.T)
+    assert g["counts"].numpy().max() <= C
+    check_layer(shape, inp, g, np.arange(shape.T), "f32")
+    # re-routing has no next-best expert under hash routing: rejected
+    cfg = moe.make_config(shape.with_(drop_tokens=False))
+    with pytest.raises(moe.MoeError):
+        moe.route_hash(cfg, shape.T, inp["token_ids"], inp["tid2eid"], x=inp["x"], w_router=inp["w_router"])
+    # a table with no rows: every slot empty, the shared expert alone remains
+    cfg = moe.make_config(shape.with_(capacity_factor=0.0))
+    empty = torch.empty((0, shape.k), dtype=torch.int32, device="cuda")
+    idx, w = moe.route_hash(cfg, shape.T, inp["token_ids"], empty, x=inp["x"], w_router=inp["w_router"])
+    torch.cuda.synchronize()
+    assert bool((idx == -1).all()) and bool((w == 0).all())
 
 
 @pytest.mark.parametrize("cf,drop", [(0.25, False), (1.25, False), (0.25, True), (1.25, True)])
