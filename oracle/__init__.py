@@ -72,6 +72,13 @@ def _load():
         lib.oracle_sqrtsoftplus32.argtypes = [ctypes.c_float]
         lib.oracle_sqrtsoftplus32_array.argtypes = [I64, P, P]
         lib.oracle_hash_select.argtypes = [P, I64, P, P, P, I64, P, P, P]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_int]
+        lib.oracle_e4m3_values.argtypes = [I64, P, P]
+        lib.oracle_quantize_e4m3.argtypes = [I64, I64, P, P, P, I64]
+        lib.oracle_forward_tokens_fp8.argtypes = [P, I64, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_router_logits.argtypes = [P, I64, P, P, P, P]
         lib.oracle_select.argtypes = [P, I64, P, P, P, P, P, P]
         lib.oracle_capacity.restype = I64
@@ -247,6 +254,61 @@ def forward_tokens(cfg, tokens, x, idx, w, get_expert):
                                        ptrs[0], ptrs[1], ptrs[2], _ptr(out))
     if rc != 0:
         raise ValueError("oracle_forward_tokens: missing expert weights")
+    return out
+
+
+def e4m3_values(codes):
+    """float64 values of E4M3 codes (NaN for the two NaN codes)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    _load().oracle_e4m3_values(codes.size, _ptr(codes), _ptr(out))
+    return out
+
+
+def e8m0_value(b):
+    return float(_load().oracle_e8m0_value(int(b)))
+
+
+def quantize_e4m3(values):
+    """fp32 [rows, K] (K % 128 == 0) -> (codes uint8 [rows, K], scale bytes
+    uint8 [rows, K/128]) in 1 x 128 tiles."""
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    if v.ndim != 2 or v.shape[1] % 128 != 0:
+        raise ValueError("values must be [rows, K] with K % 128 == 0")
+    rows, K = v.shape
+    codes = np.empty((rows, K), dtype=np.uint8)
+    scales = np.empty((rows, K // 128), dtype=np.uint8)
+    if _load().oracle_quantize_e4m3(rows, K, _ptr(v), _ptr(codes), _ptr(scales), K // 128) != 0:
+        raise ValueError("bad quantisation shape")
+    return codes, scales
+
+
+def forward_tokens_fp8(cfg, tokens, x, idx, w, get_expert):
+    """Layer output (float64 [n,H]) of the listed tokens with FP8 experts.
+    x: bf16 bits [T,H]; get_expert(e) -> (w_gate codes [I,H], gate scales
+    [I/128,H/128], w_up codes, up scales, w_down codes [H,I], down scales
+    [H/128,I/128]) as uint8 host arrays."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    n_exp = cfg.E + cfg.S
+    need = set(range(cfg.E, n_exp))
+    for t in tokens:
+        need.update(int(e) for e in idx[t] if e >= 0)
+    keep = {}
+    ptrs = [(ctypes.c_void_p * n_exp)() for _ in range(6)]
+    for e in sorted(need):
+        mats = tuple(np.ascontiguousarray(m, dtype=np.uint8) for m in get_expert(e))
+        keep[e] = mats
+        for p, m in zip(ptrs, mats):
+            p[e] = m.ctypes.data
+    out = np.empty((tokens.size, cfg.H), dtype=np.float64)
+    L = _layer(cfg)
+    rc = _load().oracle_forward_tokens_fp8(ctypes.byref(L), tokens.size, _ptr(tokens), _ptr(x), _ptr(idx), _ptr(w),
+                                           *ptrs, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_forward_tokens_fp8: missing expert weights or bad shape")
     return out
 
 

@@ -623,6 +623,176 @@ int oracle_balance_update(int E, const int32_t* counts, float* bias, float gamma
   return 0;
 }
 
+/* ---- FP8 (e4m3) experts with block scales ------------------------------------ */
+/* "15. DeepSeek：MLA、MoE 与 MTP", section "FP8 训练是训练配方，不是架构": matrix
+ * multiplication inputs in E4M3, one scale per 1 x 128 tile of activations and
+ * per 128 x 128 block of weights; V3.1 stores the scales as UE8M0 (an 8-bit
+ * exponent).  Readings: every scale (weights' and activations') is UE8M0,
+ * value 2^(b - 127); E4M3 is the format with 4 exponent bits (bias 7), 3
+ * mantissa bits, subnormals, maximum 448 and no infinities (S.1111.111 is
+ * NaN); an activation tile's scale is the smallest power of two 2^p with
+ * amax / 2^p <= 448 (p >= -127; an all-zero or subnormal-only tile takes
+ * p = -127), and each element's code is its value / 2^p rounded to the
+ * nearest E4M3 value, ties to the even mantissa, the sign kept (also on
+ * zero).  The decision is taken on fp32 values: x is bf16 (exact in fp32),
+ * the SwiGLU output h is rounded from double to fp32 first. */
+
+double oracle_e4m3_value(int c) {
+  c &= 0xFF;
+  const int e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+double oracle_e8m0_value(int b) {
+  b &= 0xFF;
+  return b == 255 ? NAN : ldexp(1.0, b - 127);
+}
+
+/* exponent p of the UE8M0 scale of a tile whose largest magnitude is amax */
+static int tile_scale_exp(float amax) {
+  if (!(amax >= 0x1p-126f)) return -127; /* zero or subnormal */
+  int ex;
+  const double f = frexp((double)amax, &ex); /* amax = f * 2^ex, f in [0.5, 1) */
+  const int E = ex - 1;                      /* amax = M * 2^E, M in [1, 2) */
+  const double M = 2.0 * f;
+  int p = E - 8 + (M > 1.75 ? 1 : 0);       /* 448 = 1.75 * 2^8 */
+  return p < -127 ? -127 : p;
+}
+
+/* nearest E4M3 code of v (|v| <= 448), ties to the even mantissa */
+static uint8_t e4m3_round(double v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0;
+  const double a = fabs(v);
+  double spacing;
+  if (a < 0x1p-6) {
+    spacing = 0x1p-9;
+  } else {
+    int ex;
+    frexp(a, &ex);
+    spacing = ldexp(1.0, ex - 1 - 3);
+  }
+  const double q = nearbyint(a / spacing); /* a / spacing is exact; rounding mode: nearest-even */
+  const double r = q * spacing;
+  if (r == 0.0) return sign;
+  if (r < 0x1p-6) return (uint8_t)(sign | (int)(r / 0x1p-9));
+  int ex;
+  frexp(r, &ex);
+  const int E = ex - 1;
+  const int m = (int)((r / ldexp(1.0, E) - 1.0) * 8.0);
+  return (uint8_t)(sign | ((E + 7) << 3) | m);
+}
+
+/* Quantise rows x K fp32 values (K % 128 == 0) in 1 x 128 tiles: codes
+ * [rows, K] and scale bytes at scales[r * scale_stride + K-tile]. */
+int oracle_quantize_e4m3(int64_t rows, int64_t K, const float* in, uint8_t* codes, uint8_t* scales,
+                         int64_t scale_stride) {
+  if (K % 128 != 0 || scale_stride < K / 128) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t kb = 0; kb < K / 128; ++kb) {
+      const float* v = in + r * K + kb * 128;
+      float amax = 0.0f;
+      for (int i = 0; i < 128; ++i)
+        if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+      const int p = tile_scale_exp(amax);
+      scales[r * scale_stride + kb] = (uint8_t)(p + 127);
+      for (int i = 0; i < 128; ++i) codes[r * K + kb * 128 + i] = e4m3_round(ldexp((double)v[i], -p));
+    }
+  return 0;
+}
+
+void oracle_e4m3_values(int64_t n, const uint8_t* codes, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_value(codes[i]);
+}
+
+/* value of element (row, col) of a block-scaled FP8 matrix [rows, cols]:
+ * code * 2^(scale[row/128, col/128] - 127) */
+static double fp8_weight(const uint8_t* codes, const uint8_t* scales, int64_t cols, int64_t row, int64_t col) {
+  return oracle_e4m3_value(codes[row * cols + col]) *
+         oracle_e8m0_value(scales[(row / 128) * (cols / 128) + col / 128]);
+}
+
+/* One expert on one token, FP8: x (bf16 bits [H]) quantised in 1 x 128
+ * tiles; g, u = dot products of the dequantised values in double; h =
+ * silu(g) * u rounded to fp32 and quantised in 1 x 128 tiles; y = W_down h
+ * over the dequantised values in double. */
+static void swiglu_row_fp8(const oracle_layer* L, const double* xq, const uint8_t* wg, const uint8_t* sg,
+                           const uint8_t* wu, const uint8_t* su, const uint8_t* wd, const uint8_t* sd, float* hbuf,
+                           uint8_t* hcodes, uint8_t* hscales, double* y) {
+  const int64_t H = L->H, I = L->I;
+  for (int64_t i = 0; i < I; ++i) {
+    double g = 0.0, u = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      g += fp8_weight(wg, sg, H, i, h) * xq[h];
+      u += fp8_weight(wu, su, H, i, h) * xq[h];
+    }
+    hbuf[i] = (float)(g * sigmoid64(g) * u);
+  }
+  oracle_quantize_e4m3(1, I, hbuf, hcodes, hscales, I / 128);
+  for (int64_t n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < I; ++i)
+      acc += fp8_weight(wd, sd, I, n, i) * oracle_e4m3_value(hcodes[i]) * oracle_e8m0_value(hscales[i / 128]);
+    y[n] = acc;
+  }
+}
+
+/* Layer output of the listed tokens with FP8 experts (as
+ * oracle_forward_tokens): x is bf16 bits [T,H]; expert e's matrices are the
+ * codes wg[e], wu[e] [I,H], wd[e] [H,I] with scale bytes sg[e], su[e]
+ * [I/128, H/128] and sd[e] [H/128, I/128]. */
+int oracle_forward_tokens_fp8(const oracle_layer* L, int64_t n_tok, const int64_t* tokens, const uint16_t* x,
+                              const int32_t* idx, const double* w, const uint8_t* const* wg, const uint8_t* const* sg,
+                              const uint8_t* const* wu, const uint8_t* const* su, const uint8_t* const* wd,
+                              const uint8_t* const* sd, double* out) {
+  const int64_t H = L->H, I = L->I;
+  const int k = L->k, E = L->E, S = L->S;
+  if (H % 128 != 0 || I % 128 != 0) return -2;
+  int bad = 0;
+#pragma omp parallel
+  {
+    float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+    uint8_t* xc = (uint8_t*)malloc((size_t)H);
+    uint8_t* xs = (uint8_t*)malloc((size_t)(H / 128));
+    double* xq = (double*)malloc(sizeof(double) * (size_t)H);
+    float* hbuf = (float*)malloc(sizeof(float) * (size_t)I);
+    uint8_t* hc = (uint8_t*)malloc((size_t)I);
+    uint8_t* hs = (uint8_t*)malloc((size_t)(I / 128));
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_tok; ++i) {
+      const int64_t t = tokens[i];
+      for (int64_t h = 0; h < H; ++h) xf[h] = (float)bf16_to_double(x[t * H + h]);
+      oracle_quantize_e4m3(1, H, xf, xc, xs, H / 128);
+      for (int64_t h = 0; h < H; ++h) xq[h] = oracle_e4m3_value(xc[h]) * oracle_e8m0_value(xs[h / 128]);
+      double* o = out + i * H;
+      for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
+      for (int j = 0; j < k + S; ++j) {
+        const int e = j < k ? idx[t * k + j] : E + (j - k);
+        if (e < 0) continue;
+        if (!wg[e] || !sg[e] || !wu[e] || !su[e] || !wd[e] || !sd[e]) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        swiglu_row_fp8(L, xq, wg[e], sg[e], wu[e], su[e], wd[e], sd[e], hbuf, hc, hs, y);
+        const double gate = j < k ? w[t * k + j] : 1.0;
+        for (int64_t n = 0; n < H; ++n) o[n] += gate * y[n];
+      }
+    }
+    free(xf);
+    free(xc);
+    free(xs);
+    free(xq);
+    free(hbuf);
+    free(hc);
+    free(hs);
+    free(y);
+  }
+  return bad ? -1 : 0;
+}
+
 /* ---- parameter arithmetic ---------------------------------------------------- */
 /* One MoE layer: router E*H plus (E+S) experts of three H x I matrices. */
 int64_t oracle_moe_layer_params(int64_t H, int64_t E, int64_t S, int64_t I) { return E * H + (E + S) * 3 * H * I; }

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_balance as B
+from tests import test_oracle_fp8 as Q
 from tests import test_oracle_ffn as F
 from tests import test_oracle_permute as P
 from tests import test_oracle_selection as S
@@ -61,6 +62,18 @@ MUTANTS = {
     "hash routing reads negative ids as row 0": ("const int64_t id = token_ids[t];",
                                                  "const int64_t id = token_ids[t] < 0 ? 0 : token_ids[t];"),
     "hash drop mode lets one token too many in": ("if (held[e] >= cap) {", "if (held[e] > cap) {"),
+    "fp8 tile scale rounded down": ("int p = E - 8 + (M > 1.75 ? 1 : 0);", "int p = E - 8;"),
+    "fp8 rounding truncates": ("const double q = nearbyint(a / spacing);", "const double q = floor(a / spacing);"),
+    "e4m3 subnormals one binade low": ("ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);",
+                                       "ldexp((double)m, -10) : ldexp((double)(8 + m), e - 10);"),
+    "fp8 weight scale of the first column block only": (
+        "oracle_e8m0_value(scales[(row / 128) * (cols / 128) + col / 128]);",
+        "oracle_e8m0_value(scales[(row / 128) * (cols / 128)]);"),
+    "fp8 h not quantised": (
+        "acc += fp8_weight(wd, sd, I, n, i) * oracle_e4m3_value(hcodes[i]) * oracle_e8m0_value(hscales[i / 128]);",
+        "acc += fp8_weight(wd, sd, I, n, i) * (double)hbuf[i];"),
+    "fp8 x not quantised": ("xq[h] = oracle_e4m3_value(xc[h]) * oracle_e8m0_value(xs[h / 128]);", "xq[h] = xf[h];"),
+    "fp8 quantised zero loses its sign": ("if (r == 0.0) return sign;", "if (r == 0.0) return 0;"),
     "group limit keeps one group too many": ("for (int i = 0; i < L->topk_group; ++i) kept[gid[i]] = 1;",
                                              "for (int i = 0; i <= L->topk_group && i < G; ++i) kept[gid[i]] = 1;"),
     "permutation in descending token order": ("for (int e = 0; e < E; ++e) fill[e] = offsets[e];\n  for (int64_t t = 0; t < T; ++t) {",
@@ -88,6 +101,10 @@ PINS = [
     V.test_bias_changes_selection_but_not_gates, V.test_hash_routing_hand_example,
     V.test_hash_routing_follows_the_table_whatever_the_logits,
     V.test_hash_routing_drop_mode_keeps_the_first_c_assignments,
+    Q.test_e4m3_decode_hand_values, Q.test_quantize_hand_tiles,
+    lambda: Q.test_quantize_matches_torch_rounding_and_minimal_scale(0),
+    Q.test_fp8_layer_matches_block_expansion_with_library_rounding,
+    Q.test_fp8_layer_with_exact_inputs_is_the_bf16_layer_up_to_h_rounding,
     B.test_loads_at_the_mean_keep_their_bias, B.test_random_loads_against_library_entropy_and_float32_steps,
     F.test_swiglu_closed_form_with_selection_matrices, F.test_single_expert_layer_is_a_dense_swiglu_ffn,
     F.test_identical_experts_factor_out, F.test_empty_slots_are_skipped_and_bf16_inputs_are_exact,

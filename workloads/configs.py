@@ -23,7 +23,8 @@ class LayerShape:
     scale: float = 1.0          # routed scaling factor applied to the gates
     capacity_factor: float = 0.0  # <= 0: unlimited
     drop_tokens: bool = False   # with a capacity: drop overflow instead of re-routing
-    dtype: str = "bf16"         # "bf16" | "f32" for x and every weight
+    dtype: str = "bf16"         # "bf16" | "f32" for x and every weight; "fp8": bf16 x and
+                                # router, E4M3 expert weights with 128 x 128 UE8M0 block scales
     sel_bias: Optional[float] = None   # selection bias ~ U(-a, a) when set
     zipf_s: Optional[float] = None     # Zipf exponent of the per-expert logit offset
     hash_vocab: int = 0         # > 0: hash routing through a [hash_vocab, k] token-id table

@@ -2,7 +2,8 @@
 
 Distributions: x ~ N(0, 1); every weight ~ N(0, 1/fan_in) (router and gate/up:
 fan_in = H; down: fan_in = I); optional selection bias ~ U(-a, a) in fp32;
-optional Zipf(s) per-expert logit offset; for hash routing, token ids with
+optional Zipf(s) per-expert logit offset; FP8-expert layers draw E4M3 codes
+and UE8M0 block scales instead of bf16 expert weights; for hash routing, token ids with
 Zipf(1) frequencies over the vocabulary and a table of k distinct uniformly
 drawn experts per id.  bf16 tensors are produced by
 rounding fp32 draws to nearest-even (torch's conversion).
@@ -18,7 +19,8 @@ import math
 import numpy as np
 import torch
 
-_TENSORS = ("x", "w_router", "sel_bias", "zipf_perm", "w_gate", "w_up", "w_down", "token_ids", "tid2eid")
+_TENSORS = ("x", "w_router", "sel_bias", "zipf_perm", "w_gate", "w_up", "w_down", "token_ids", "tid2eid",
+            "s_gate", "s_up", "s_down")
 
 
 def _seed(base: int, name: str) -> int:
@@ -32,7 +34,23 @@ def _gen(device, base: int, name: str) -> torch.Generator:
 
 
 def _dtype(cfg):
+    """dtype of x and the router weight (bf16 for FP8-expert layers)."""
     return torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+
+def _fp8_matrix(shape, fan_in, g_codes, g_scales, device):
+    """E4M3 codes [E+S, rows, cols] (uint8) and UE8M0 block scales [E+S,
+    rows/128, cols/128]: codes of 40 * N(0,1) draws (torch's float8_e4m3fn
+    conversion), block exponents 2^-(6 + log2 sqrt(fan_in)) +- 1 at random, so
+    the values have about the spread of N(0, 1/fan_in)."""
+    n, rows, cols = shape
+    codes = torch.empty(shape, dtype=torch.uint8, device=device)
+    for e in range(n):
+        t = torch.randn((rows, cols), generator=g_codes, device=device, dtype=torch.float32).mul_(40.0)
+        codes[e] = t.to(torch.float8_e4m3fn).view(torch.uint8)
+    base = 127 - 6 - int(round(math.log2(math.sqrt(fan_in))))
+    jitter = torch.randint(-1, 2, (n, rows // 128, cols // 128), generator=g_scales, device=device)
+    return codes, (jitter + base).to(torch.uint8)
 
 
 def _normal(shape, std, g, device, dtype):
@@ -77,7 +95,9 @@ def zipf_token_ids(T: int, vocab: int, seed: int, s: float = 1.0) -> np.ndarray:
 def make_inputs(cfg, device="cpu", seed=None, T=None):
     """Return a dict of tensors on `device`:
     x [T,H], w_router [E,H], w_gate/w_up [E+S,I,H], w_down [E+S,H,I] in the
-    layer dtype; sel_bias [E] fp32 or None; logit_bias [E] fp32 or None;
+    layer dtype (FP8-expert layers: x and w_router bf16, the expert matrices
+    E4M3 codes with s_gate/s_up [E+S,I/128,H/128] and s_down [E+S,H/128,I/128]
+    UE8M0 block scales); sel_bias [E] fp32 or None; logit_bias [E] fp32 or None;
     with hash routing token_ids [T] and tid2eid [vocab,k] int32, else None."""
     base = cfg.seed if seed is None else seed
     T = cfg.T if T is None else T
@@ -102,6 +122,12 @@ def make_inputs(cfg, device="cpu", seed=None, T=None):
         out["tid2eid"] = torch.from_numpy(hash_table(vocab, E, cfg.k, base)).to(device)
     else:
         out["token_ids"] = out["tid2eid"] = None
+    if cfg.dtype == "fp8":
+        for name, sname, shape, fan in (("w_gate", "s_gate", (I, H), H), ("w_up", "s_up", (I, H), H),
+                                        ("w_down", "s_down", (H, I), I)):
+            out[name], out[sname] = _fp8_matrix((E + S,) + shape, fan, _gen(device, base, name),
+                                                _gen(device, base, sname), device)
+        return out
     for name, shape, std in (("w_gate", (I, H), 1.0 / math.sqrt(H)),
                              ("w_up", (I, H), 1.0 / math.sqrt(H)),
                              ("w_down", (H, I), 1.0 / math.sqrt(I))):
