@@ -1,14 +1,17 @@
 """Benchmark of the MoE layer on one MI355X.
 
-One step = one moe_forward call (moe_forward_hash for hash-routed workloads):
-router, capacity when configured, permute, gate/up+SwiGLU GEMM, down GEMM,
-combine, over one batch of seeded synthetic inputs already resident in HBM.  Default workload: the DeepSeek-V3-shaped
-prefill layer (16384 tokens, hidden 7168, 256 routed + 1 shared experts,
-top-8 of 8 groups / 4 kept, intermediate 2048, bf16).
+One step = one layer call over one batch of seeded synthetic inputs already
+resident in HBM: moe_forward (moe_forward_hash for hash-routed workloads,
+moe_forward_fp8 for FP8-expert workloads), i.e. router, capacity when
+configured, permute, (FP8: activation quantisation,) gate/up+SwiGLU GEMM,
+down GEMM, combine.  Default workload: the DeepSeek-V3-shaped prefill layer
+(16384 tokens, hidden 7168, 256 routed + 1 shared experts, top-8 of 8 groups
+/ 4 kept, intermediate 2048, bf16).
 
 Prints one JSON line: tokens/s of the whole job, the roofline of the dominant
-kernel (gate/up + SwiGLU grouped GEMM, bf16 MFMA) timed live with HIP events
-on the launch stream, and the CPU oracle timed on a bounded token sample.
+kernel (gate/up + SwiGLU grouped GEMM on the bf16 or fp8 matrix cores) timed
+live with HIP events on the launch stream, and the CPU oracle timed on a
+bounded token sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
 """
@@ -25,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at DeepSeek-V3 shape; % bf16 MFMA peak / % HBM BW"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "routing_expert_ffn_amd", "csrc", "gemm.hip")
 
@@ -69,6 +73,7 @@ def cpu_baseline(shape, inp, target_s):
     lb = to_oracle(inp["logit_bias"])
     wg, wu, wd = to_oracle(inp["w_gate"]), to_oracle(inp["w_up"]), to_oracle(inp["w_down"])
     ids, tab = to_oracle(inp["token_ids"]), to_oracle(inp["tid2eid"])
+    sg, su, sd = (to_oracle(inp.get(n)) for n in ("s_gate", "s_up", "s_down"))
     torch.cuda.synchronize()
     rng = np.random.default_rng(77)
     order = rng.permutation(shape.T)
@@ -80,7 +85,11 @@ def cpu_baseline(shape, inp, target_s):
             idx, w, _ = oracle.hash_select(shape, logits, ids[tokens], tab)
         else:
             idx, w, _, _ = oracle.select(shape, logits, sb)
-        oracle.forward_tokens(shape, np.arange(len(tokens)), x[tokens], idx, w, lambda e: (wg[e], wu[e], wd[e]))
+        if shape.dtype == "fp8":
+            oracle.forward_tokens_fp8(shape, np.arange(len(tokens)), x[tokens], idx, w,
+                                      lambda e: (wg[e], sg[e], wu[e], su[e], wd[e], sd[e]))
+        else:
+            oracle.forward_tokens(shape, np.arange(len(tokens)), x[tokens], idx, w, lambda e: (wg[e], wu[e], wd[e]))
         return time.perf_counter() - t0
 
     n1 = max(cores, 4)
@@ -141,7 +150,11 @@ def main():
         log("calibration: 3 device copies of 1 GiB")
 
     def step():
-        if inp["tid2eid"] is not None:
+        if shape.dtype == "fp8":
+            moe.forward_fp8(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["s_gate"], inp["w_up"], inp["s_up"],
+                            inp["w_down"], inp["s_down"], logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"],
+                            out=out, topk_idx=idx, expert_counts=counts, ws=ws)
+        elif inp["tid2eid"] is not None:
             moe.forward_hash(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
                              inp["token_ids"], inp["tid2eid"], logit_bias=inp["logit_bias"], out=out, topk_idx=idx,
                              expert_counts=counts, ws=ws)
@@ -179,7 +192,11 @@ def main():
     gu_ms = kernels.get("gateup_swiglu")
     achieved = gateup_flops / (gu_ms * 1e-3) / 1e12
     touched = int((counts > 0).sum().item())
-    weight_bytes = (touched + shape.S) * 3 * shape.H * shape.I * (2 if shape.dtype == "bf16" else 4)
+    wsz = {"fp8": 1, "bf16": 2, "f32": 4}[shape.dtype]
+    weight_bytes = (touched + shape.S) * 3 * shape.H * shape.I * wsz
+    if shape.dtype == "fp8":  # plus the UE8M0 block scales
+        weight_bytes += (touched + shape.S) * 3 * (shape.H // 128) * (shape.I // 128)
+    peak = PEAK_FP8_TFLOPS if shape.dtype == "fp8" else PEAK_BF16_TFLOPS
     res = {
         "metric": METRIC,
         "value": T / (ms_step * 1e-3),
@@ -197,11 +214,11 @@ def main():
                    "shared_experts": shape.S, "top_k": shape.k, "groups": shape.G, "groups_kept": shape.topk_group,
                    "intermediate": shape.I, "scoring": shape.scoring, "capacity_factor": shape.capacity_factor,
                    "routing": "hash" if shape.hash_vocab else "learned", "out_dtype": "bf16"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(shape.name),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": measured_traffic(shape.name),
                      "kernel": "gateup_swiglu", "flops_per_launch": gateup_flops, "ms_per_launch": gu_ms},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
-        "layer_mfma_frac": layer_flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "layer_mfma_frac": layer_flops / (ms_step * 1e-3) / 1e12 / peak,
         "layer_weight_gbs": weight_bytes / (ms_step * 1e-3) / 1e9,
         "layer_hbm_frac": weight_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels_ms": kernels,

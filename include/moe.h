@@ -21,13 +21,17 @@
  *                   ("MoE on KnightLi的博客", activation functions; DeepSeek page,
  *                   "671B 和 37B 的参数账")
  *   combine         out = sum_j w_j * expert_{idx_j}(x) + sum_s shared_s(x)
+ *   FP8 experts     E4M3 matrices, UE8M0 scales per 128 x 128 weight block and
+ *                   per 1 x 128 activation tile   DeepSeek page, "FP8 训练是训练配方，不是架构"
  *
  * Conventions shared by every call
  *  - Every pointer argument that names a tensor is a DEVICE pointer on the
  *    current HIP device, owned by the caller, row-major and densely packed.
  *    The library allocates no device memory and keeps no device state.
  *  - "Input dtype" (moe_config.dtype) applies to x and every weight matrix:
- *    MOE_BF16 (bfloat16) or MOE_F32.  Logits, gates and biases are fp32.
+ *    MOE_BF16 (bfloat16) or MOE_F32; MOE_FP8 layers take bf16 x and router
+ *    weight and E4M3 expert matrices with block scales (moe_forward_fp8).
+ *    Logits, gates and biases are fp32.
  *  - Matrices keep their reduction dimension contiguous: w_router [E,H],
  *    w_gate/w_up [E+S,I,H], w_down [E+S,H,I]; routed experts 0..E-1 first,
  *    shared experts E..E+S-1 after them.
@@ -65,7 +69,10 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SQRTSOFTPLUS = 2 } moe_scoring;
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_FP8: x and the router weight are bf16; the expert matrices are E4M3
+ * codes with one UE8M0 scale per 128 x 128 block (moe_forward_fp8,
+ * moe_expert_ffn_fp8). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8 = 2 } moe_dtype;
 
 /* Layer description: the fields the DeepSeek page reads from a checkpoint's
  * config (n_routed_experts, n_shared_experts, num_experts_per_tok, n_group,
@@ -84,7 +91,8 @@ typedef struct moe_config {
   int32_t norm_topk_prob;        /* 1: gates renormalised over the selection     */
   float routed_scaling_factor;   /* multiplies every routed gate (2.5 for V3)    */
   float capacity_factor;         /* <= 0: unlimited; else C = ceil(cf*T*k/E)    */
-  int32_t dtype;                 /* moe_dtype of x and every weight              */
+  int32_t dtype;                 /* moe_dtype of x and every weight (MOE_FP8: see
+                                    moe_dtype)                                    */
   int32_t out_dtype;             /* moe_dtype of `out`                            */
   int32_t drop_tokens;           /* with a capacity: 1 = drop the overflow, 0 =
                                     re-route it to the next-best allowed expert */
@@ -201,6 +209,43 @@ moe_status moe_forward_hash(const moe_config* cfg, int64_t T, const void* x, con
                             const void* w_gate, const void* w_up, const void* w_down, void* out, int32_t* topk_idx,
                             float* topk_w, int32_t* expert_counts, float* logits_out, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* FP8 experts ("15. DeepSeek：MLA、MoE 与 MTP", section "FP8 训练是训练配方，不是架构":
+ * E4M3 inputs of the matrix products, one scale per 1 x 128 activation tile
+ * and per 128 x 128 weight block, UE8M0 scales as in V3.1).  cfg->dtype must
+ * be MOE_FP8.
+ *   x            [T,H] bf16;  w_router [E,H] bf16
+ *   w_gate, w_up [E+S,I,H] E4M3 codes (1 byte: sign, 4 exponent bits with
+ *                bias 7, 3 mantissa bits; subnormals; 0x7F/0xFF are NaN)
+ *   s_gate, s_up [E+S,I/128,H/128] UE8M0 bytes b: the block's scale is
+ *                2^(b-127) (b = 255 is not allowed)
+ *   w_down       [E+S,H,I] E4M3 codes;  s_down [E+S,H/128,I/128] UE8M0
+ * Element (r,c) of an expert matrix is code(r,c) * 2^(b(r/128,c/128) - 127).
+ * x and the SwiGLU output h are quantised per row and 128-wide tile as
+ * moe_quantize_fp8 describes (h from its fp32 value); the products run on the
+ * matrix cores with the scales applied per 128-wide K block and fp32
+ * accumulation.  Everything else (routing, capacity, combine, outputs,
+ * workspace) as moe_forward / moe_expert_ffn. */
+moe_status moe_forward_fp8(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                           const float* logit_bias, const float* sel_bias, const uint8_t* w_gate, const uint8_t* s_gate,
+                           const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                           void* out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts, float* logits_out,
+                           void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_ffn_fp8(const moe_config* cfg, int64_t T, const void* x, const uint8_t* w_gate,
+                              const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
+                              const uint8_t* s_down, const int32_t* expert_offsets, const int32_t* row_token,
+                              void* y_rows, void* ws, size_t ws_bytes, void* stream);
+/* 1 x 128 tile quantisation of bf16 rows to E4M3 (the activation format of
+ * the FP8 experts).
+ *   in      [rows,K] bf16 device, 16-byte aligned; K a positive multiple of 128
+ *   codes   [rows,K] E4M3 out, 8-byte aligned
+ *   scales  [rows, scale_stride] UE8M0 out; tile j of row r at r*scale_stride + j
+ * A tile's scale is 2^p for the smallest p >= -127 with amax/2^p <= 448
+ * (p = -127 when amax is zero or subnormal); each code is value/2^p rounded
+ * to the nearest E4M3 value, ties to the even mantissa, sign kept (also on
+ * zero).  Bytes of scales past K/128 in a row are left untouched. */
+moe_status moe_quantize_fp8(int64_t rows, int32_t K, const void* in, uint8_t* codes, uint8_t* scales,
+                            int32_t scale_stride, void* stream);
 
 /* One step of auxiliary-loss-free load balancing ("15. DeepSeek：MLA、MoE 与
  * MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the bias paragraph) and the

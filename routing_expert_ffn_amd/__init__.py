@@ -14,15 +14,16 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 SCORING = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID, "sqrtsoftplus": MOE_SCORE_SQRTSOFTPLUS}
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
           -4: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_hash", "moe_balance_update", "moe_last_error", "moe_version",
-           "moe_timing_enable", "moe_timing_read", "moe_kernel_name")
+           "moe_forward", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8", "moe_quantize_fp8",
+           "moe_balance_update", "moe_last_error", "moe_version", "moe_timing_enable", "moe_timing_read",
+           "moe_kernel_name")
 
 
 class MoeError(RuntimeError):
@@ -44,8 +45,11 @@ def make_config(shape, out_dtype=None):
     """moe_config from a layer description (attributes H, E, S, k, G,
     topk_group, I, scoring, renorm, scale, capacity_factor, dtype and
     optionally drop_tokens)."""
-    dt = MOE_F32 if shape.dtype == "f32" else MOE_BF16
-    od = dt if out_dtype is None else (MOE_F32 if out_dtype in ("f32", torch.float32, MOE_F32) else MOE_BF16)
+    dt = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8}[shape.dtype]
+    if out_dtype is None:
+        od = MOE_F32 if dt == MOE_F32 else MOE_BF16
+    else:
+        od = MOE_F32 if out_dtype in ("f32", torch.float32, MOE_F32) else MOE_BF16
     return moe_config(shape.H, shape.E, shape.S, shape.k, shape.G, shape.topk_group, shape.I,
                       SCORING[shape.scoring],
                       1 if shape.renorm else 0, float(shape.scale), float(shape.capacity_factor), dt, od,
@@ -67,8 +71,8 @@ def lib():
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         C = ctypes.POINTER(moe_config)
         for name in ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn",
-                     "moe_combine", "moe_forward", "moe_forward_hash", "moe_balance_update", "moe_timing_enable",
-                     "moe_timing_read"):
+                     "moe_combine", "moe_forward", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8",
+                     "moe_quantize_fp8", "moe_balance_update", "moe_timing_enable", "moe_timing_read"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [C, I64, ctypes.POINTER(SZ)]
         L.moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -79,6 +83,9 @@ def lib():
         L.moe_forward.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_route_hash.argtypes = [C, I64, P, P, P, P, P, P, P, I64, P, P, P, P, SZ, P]
         L.moe_forward_hash.argtypes = [C, I64, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_forward_fp8.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_expert_ffn_fp8.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_quantize_fp8.argtypes = [I64, I32, P, P, P, I32, P]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_version.restype = ctypes.c_char_p
@@ -238,6 +245,49 @@ def forward_hash(cfg, x, w_router, w_gate, w_up, w_down, token_ids, tid2eid, log
                                   _p(topk_idx), _p(topk_w), _p(expert_counts), _p(logits_out), _p(ws), ws.numel(),
                                   _stream(stream)))
     return out
+
+
+def forward_fp8(cfg, x, w_router, w_gate, s_gate, w_up, s_up, w_down, s_down, logit_bias=None, sel_bias=None,
+                out=None, topk_idx=None, topk_w=None, expert_counts=None, logits_out=None, ws=None, stream=None):
+    """The whole layer with FP8 experts (uint8 E4M3 codes and UE8M0 block
+    scales); -> out [T,H] in cfg.out_dtype."""
+    T = x.shape[0]
+    if out is None:
+        dt = torch.float32 if cfg.out_dtype == MOE_F32 else torch.bfloat16
+        out = torch.empty((T, cfg.hidden_size), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(cfg, T, x.device)
+    _check(lib().moe_forward_fp8(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(sel_bias),
+                                 _p(w_gate), _p(s_gate), _p(w_up), _p(s_up), _p(w_down), _p(s_down), _p(out),
+                                 _p(topk_idx), _p(topk_w), _p(expert_counts), _p(logits_out), _p(ws), ws.numel(),
+                                 _stream(stream)))
+    return out
+
+
+def expert_ffn_fp8(cfg, x, w_gate, s_gate, w_up, s_up, w_down, s_down, expert_offsets, row_token, y_rows=None,
+                   ws=None, stream=None):
+    """-> y_rows [T*k+S*T, H] fp32 (FP8 experts)"""
+    T = x.shape[0]
+    rows = T * cfg.top_k + cfg.n_shared_experts * T
+    if y_rows is None:
+        y_rows = torch.empty((rows, cfg.hidden_size), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(cfg, T, x.device)
+    _check(lib().moe_expert_ffn_fp8(ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(s_gate), _p(w_up), _p(s_up),
+                                    _p(w_down), _p(s_down), _p(expert_offsets), _p(row_token), _p(y_rows), _p(ws),
+                                    ws.numel(), _stream(stream)))
+    return y_rows
+
+
+def quantize_fp8(x, scale_stride=None, stream=None):
+    """bf16 [rows, K] -> (E4M3 codes uint8 [rows, K], UE8M0 scales uint8
+    [rows, scale_stride]) in 1 x 128 tiles."""
+    rows, K = x.shape
+    ss = K // 128 if scale_stride is None else scale_stride
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    scales = torch.zeros((rows, ss), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quantize_fp8(rows, K, _p(x), _p(codes), _p(scales), ss, _stream(stream)))
+    return codes, scales
 
 
 def timing_enable(max_launches):

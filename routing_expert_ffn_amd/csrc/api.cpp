@@ -55,7 +55,9 @@ struct Dims {
   int capacity;   // <= 0: unlimited
   int drop;       // with a capacity: drop the overflow instead of re-routing
   int n_allowed;
-  int esz;        // bytes per input element
+  int esz;        // bytes per element of x (and the router weight)
+  int xdt;        // dtype of x and the router weight: MOE_F32 or MOE_BF16
+  int fp8;        // expert matrices are E4M3 codes with UE8M0 block scales
 };
 
 moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
@@ -74,7 +76,8 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
   d.scale = c->routed_scaling_factor;
   d.dtype = c->dtype;
   d.out_dtype = c->out_dtype;
-  if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32 or MOE_BF16");
+  if (d.dtype != MOE_F32 && d.dtype != MOE_BF16 && d.dtype != MOE_FP8)
+    return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32, MOE_BF16 or MOE_FP8");
   if (d.out_dtype != MOE_F32 && d.out_dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_F32 or MOE_BF16");
   if (d.scoring != MOE_SCORE_SOFTMAX && d.scoring != MOE_SCORE_SIGMOID && d.scoring != MOE_SCORE_SQRTSOFTPLUS)
@@ -94,14 +97,17 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
   if (d.k > d.n_allowed) return fail(MOE_ERR_INVALID_ARG, "top_k exceeds the experts of the kept groups");
   if (!std::isfinite(d.scale)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling_factor must be finite");
   if (!std::isfinite(c->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
-  if (d.dtype == MOE_BF16) {
-    if (d.H % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need hidden_size % 256 == 0");
-    if (d.I % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need moe_intermediate_size % 128 == 0");
+  if (d.dtype != MOE_F32) {
+    if (d.H % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 and FP8 layers need hidden_size % 256 == 0");
+    if (d.I % 128 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 and FP8 layers need moe_intermediate_size % 128 == 0");
   } else {
     if (d.H % 32 != 0) return fail(MOE_ERR_UNSUPPORTED, "fp32 layers need hidden_size % 32 == 0");
     if (d.I % 32 != 0) return fail(MOE_ERR_UNSUPPORTED, "fp32 layers need moe_intermediate_size % 32 == 0");
   }
-  d.esz = d.dtype == MOE_BF16 ? 2 : 4;
+  d.fp8 = d.dtype == MOE_FP8 ? 1 : 0;
+  d.xdt = d.dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+  d.esz = d.xdt == MOE_BF16 ? 2 : 4;
   const int64_t rows = T * d.k + (int64_t)d.S * T;
   if (rows > 0x7FFFFFFF || T * (int64_t)d.E > 0x7FFFFFFF)
     return fail(MOE_ERR_UNSUPPORTED, "T*(k+S) and T*E must fit in int32");
@@ -120,8 +126,12 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
 
 struct Layout {
   size_t logits, rpart, cand, idx, w, counts, offsets, slot_row, row_token, chunk_cnt, chunk_base, seg_start, seg_len,
-      f_prefix, h_prefix, h, y, total;
+      f_prefix, h_prefix, h, y, xq, sx, sh, total;
 };
+
+// FP8 layers: row strides of the activation scale arrays (bytes)
+int sx_stride(const Dims& d) { return d.H / 128; }
+int sh_stride(const Dims& d) { return d.I / 128; }
 
 Layout layout_of(const Dims& d) {
   Layout L{};
@@ -137,7 +147,7 @@ Layout layout_of(const Dims& d) {
   L.logits = take(T * E * 4);
   // partial router logits of the K slices (bf16 router GEMM, small T)
   size_t nsplit = 1;
-  if (d.dtype == MOE_BF16 && d.T > 0) {
+  if (d.xdt == MOE_BF16 && d.T > 0) {
     int sps;
     nsplit = (size_t)router_splits(d.T, d.H, &sps);
   }
@@ -155,8 +165,12 @@ Layout layout_of(const Dims& d) {
   L.seg_len = take((E + S) * 4);
   L.f_prefix = take((E + S + 1) * 4);
   L.h_prefix = take((E + S + 1) * 4);
-  L.h = take(rows * (size_t)d.I * d.esz);
+  L.h = take(rows * (size_t)d.I * (d.fp8 ? 1 : d.esz));  // FP8: E4M3 codes of h
   L.y = take(rows * (size_t)d.H * 4);  // expert outputs are fp32
+  // FP8: x's codes and the scales of x and h
+  L.xq = take(d.fp8 ? T * (size_t)d.H : 0);
+  L.sx = take(d.fp8 ? T * (size_t)sx_stride(d) : 0);
+  L.sh = take(d.fp8 ? rows * (size_t)sh_stride(d) : 0);
   L.total = off;
   return L;
 }
@@ -204,7 +218,7 @@ RouteParams route_params(const Dims& d) {
 hipError_t run_router(const Dims& d, RouterArgs a, const void* x, const void* w_router, void* ws, const Layout& L,
                       hipStream_t s) {
   if (a.logits_in) return timed(K_ROUTE_SELECT, s, [&] { return launch_route_select(a, s); });
-  if (d.dtype != MOE_BF16) return timed(K_ROUTER, s, [&] { return launch_router(a, d.dtype, s); });
+  if (d.xdt != MOE_BF16) return timed(K_ROUTER, s, [&] { return launch_router(a, d.xdt, s); });
   int sps;
   const int S = router_splits(d.T, d.H, &sps);
   float* lg = a.logits_out ? a.logits_out : at<float>(ws, L.logits);
@@ -348,12 +362,32 @@ moe_status do_permute(const Dims& d, const int32_t* topk_idx, int32_t* counts, i
   return MOE_OK;
 }
 
-// Expert FFNs: y_rows [T*k+S*T, H] fp32; or, with y16 set (bf16 layers inside
-// moe_forward), the routed rows [T*k, H] in bf16 to y16 and the shared rows
-// [S*T, H] fp32 to y_rows.
+// UE8M0 block scales of FP8 expert matrices.
+struct Fp8Scales {
+  const uint8_t* gate;  // [E+S, I/128, H/128]
+  const uint8_t* up;    // [E+S, I/128, H/128]
+  const uint8_t* down;  // [E+S, H/128, I/128]
+};
+
+// Expert FFNs: y_rows [T*k+S*T, H] fp32; or, with y16 set (bf16 and FP8
+// layers inside moe_forward), the routed rows [T*k, H] in bf16 to y16 and the
+// shared rows [S*T, H] fp32 to y_rows.  FP8 layers (f8 set) first quantise x
+// in 1 x 128 tiles into the workspace.
 moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* w_up, const void* w_down,
                   const int32_t* offsets, const int32_t* row_token, void* y_rows, void* ws, const Layout& L,
-                  hipStream_t s, void* y16 = nullptr) {
+                  hipStream_t s, void* y16 = nullptr, const Fp8Scales* f8 = nullptr) {
+  hipError_t e;
+  if (f8) {
+    QuantArgs q{};
+    q.rows = d.T;
+    q.K = d.H;
+    q.in = x;
+    q.codes = at<uint8_t>(ws, L.xq);
+    q.scales = at<uint8_t>(ws, L.sx);
+    q.sstride = sx_stride(d);
+    e = timed(K_QUANT, s, [&] { return launch_quantize_fp8(q, s); });
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  }
   const int BM = gemm_bm(d.dtype);
   ScheduleArgs sa{};
   sa.T = (int)d.T;
@@ -367,7 +401,7 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   sa.seg_len = at<int32_t>(ws, L.seg_len);
   sa.f_prefix = at<int32_t>(ws, L.f_prefix);
   sa.h_prefix = at<int32_t>(ws, L.h_prefix);
-  hipError_t e = timed(K_SCHEDULE, s, [&] { return launch_schedule(sa, s); });
+  e = timed(K_SCHEDULE, s, [&] { return launch_schedule(sa, s); });
   if (e != hipSuccess) return hip_fail(e, "schedule launch");
   const int64_t bound = gemm_mtile_bound((int)d.T, d.E, d.S, d.k, BM);
   GemmArgs g{};
@@ -381,21 +415,37 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   // gate/up + SwiGLU
   g.K = d.H;
   g.N = d.I;
-  g.n_tiles = d.dtype == MOE_BF16 ? d.I / 128 : d.I / 32;
+  g.n_tiles = d.dtype != MOE_F32 ? d.I / 128 : d.I / 32;
   g.a = x;
   g.b0 = w_gate;
   g.b1 = w_up;
   g.c = h;
+  if (f8) {
+    g.a = at<uint8_t>(ws, L.xq);
+    g.sa = at<uint8_t>(ws, L.sx);
+    g.sa_stride = sx_stride(d);
+    g.sb0 = f8->gate;
+    g.sb1 = f8->up;
+    g.sc = at<uint8_t>(ws, L.sh);
+    g.sc_stride = sh_stride(d);
+  }
   if (bound * g.n_tiles > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "too many GEMM tiles");
   e = timed(K_GATEUP, s, [&] { return launch_gateup(g, d.dtype, bound, s); });
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
   // down
   g.K = d.I;
   g.N = d.H;
-  g.n_tiles = d.dtype == MOE_BF16 ? d.H / 256 : d.H / 32;
+  g.n_tiles = d.dtype != MOE_F32 ? d.H / 256 : d.H / 32;
   g.a = h;
   g.b0 = w_down;
   g.b1 = nullptr;
+  if (f8) {
+    g.sa = at<uint8_t>(ws, L.sh);
+    g.sa_stride = sh_stride(d);
+    g.sb0 = f8->down;
+    g.sb1 = nullptr;
+    g.sc = nullptr;
+  }
   g.c = y_rows;
   g.c16 = y16;
   g.n_routed = d.E;
@@ -425,13 +475,18 @@ moe_status do_combine(const Dims& d, const void* y_routed, bool routed_bf16, con
   return MOE_OK;
 }
 
-// The whole layer (learned routing, or hash routing when `hash` is set).
+// The whole layer (learned routing, or hash routing when `hash` is set; FP8
+// expert matrices when `f8` is set).
 moe_status forward_impl(const Dims& d, const void* x, const void* w_router, const float* logit_bias,
                         const float* sel_bias, const void* w_gate, const void* w_up, const void* w_down, void* out,
                         int32_t* topk_idx, float* topk_w, int32_t* expert_counts, float* logits_out, void* ws,
-                        size_t ws_bytes, hipStream_t s, const HashTable* hash) {
+                        size_t ws_bytes, hipStream_t s, const HashTable* hash, const Fp8Scales* f8 = nullptr) {
   moe_status st;
+  if (d.fp8 != (f8 != nullptr))
+    return fail(MOE_ERR_INVALID_ARG, d.fp8 ? "MOE_FP8 layers run through moe_forward_fp8"
+                                           : "moe_forward_fp8 needs dtype MOE_FP8");
   if (d.T == 0) return MOE_OK;
+  if (f8 && (!f8->gate || !f8->up || !f8->down)) return fail(MOE_ERR_INVALID_ARG, "NULL scale argument");
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
       !aligned16(out))
@@ -450,7 +505,7 @@ moe_status forward_impl(const Dims& d, const void* x, const void* w_router, cons
   if (st != MOE_OK) return st;
   st = do_permute(d, idx, counts, offsets, row_token, slot_row, ws, L, s);
   if (st != MOE_OK) return st;
-  if (d.dtype == MOE_BF16 && d.S >= 1) {
+  if (d.dtype != MOE_F32 && d.S >= 1) {
     // routed expert rows in bf16, shared expert rows in fp32, in the
     // expert-row region: with a shared expert, whose unweighted fp32 row
     // carries much of each output, the bf16 rounding of the gate-weighted
@@ -459,11 +514,11 @@ moe_status forward_impl(const Dims& d, const void* x, const void* w_router, cons
     // output is a sum of rounded rows and all rows stay fp32
     void* y16 = y;
     float* y32 = reinterpret_cast<float*>(static_cast<char*>(y) + (size_t)d.T * d.k * d.H * 2);
-    st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y32, ws, L, s, y16);
+    st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y32, ws, L, s, y16, f8);
     if (st != MOE_OK) return st;
     return do_combine(d, y16, true, y32, slot_row, w, out, s);
   }
-  st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y, ws, L, s);
+  st = do_ffn(d, x, w_gate, w_up, w_down, offsets, row_token, y, ws, L, s, nullptr, f8);
   if (st != MOE_OK) return st;
   return do_combine(d, y, false, static_cast<const float*>(y) + (int64_t)d.T * d.k * d.H, slot_row, w, out, s);
 }
@@ -474,7 +529,8 @@ moe_status forward_impl(const Dims& d, const void* x, const void* w_router, cons
 const char* kernel_name(int id) {
   static const char* names[K_COUNT] = {"fill",          "router",          "router_select", "capacity",
                                        "permute_count", "permute_scan",    "permute_scatter", "schedule",
-                                       "gateup_swiglu", "down",            "combine",         "balance"};
+                                       "gateup_swiglu", "down",            "combine",         "balance",
+                                       "quantize"};
   return (id >= 0 && id < K_COUNT) ? names[id] : nullptr;
 }
 
@@ -504,7 +560,7 @@ moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void
   Layout L{};
   // the workspace holds the capacity candidates, and for bf16 layers the
   // router GEMM's logits and K-slice partials
-  if (d.capacity > 0 || (!logits_in && d.dtype == MOE_BF16)) {
+  if (d.capacity > 0 || (!logits_in && d.xdt == MOE_BF16)) {
     st = check_ws(d, ws, ws_bytes, L);
     if (st != MOE_OK) return st;
   }
@@ -545,10 +601,53 @@ moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const
     return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(y_rows))
     return fail(MOE_ERR_INVALID_ARG, "x, weights and y_rows must be 16-byte aligned");
+  if (d.fp8) return fail(MOE_ERR_INVALID_ARG, "MOE_FP8 layers run through moe_expert_ffn_fp8");
   Layout L{};
   st = check_ws(d, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
   return do_ffn(d, x, w_gate, w_up, w_down, expert_offsets, row_token, y_rows, ws, L, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn_fp8(const moe_config* cfg, int64_t T, const void* x, const uint8_t* w_gate,
+                              const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
+                              const uint8_t* s_down, const int32_t* expert_offsets, const int32_t* row_token,
+                              void* y_rows, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  if (!d.fp8) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_fp8 needs dtype MOE_FP8");
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate || !w_up || !w_down || !s_gate || !s_up || !s_down || !expert_offsets || !row_token || !y_rows)
+    return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(y_rows))
+    return fail(MOE_ERR_INVALID_ARG, "x, weights and y_rows must be 16-byte aligned");
+  Layout L{};
+  st = check_ws(d, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  const Fp8Scales f8{s_gate, s_up, s_down};
+  return do_ffn(d, x, w_gate, w_up, w_down, expert_offsets, row_token, y_rows, ws, L, static_cast<hipStream_t>(stream),
+                nullptr, &f8);
+}
+
+moe_status moe_quantize_fp8(int64_t rows, int32_t K, const void* in, uint8_t* codes, uint8_t* scales,
+                            int32_t scale_stride, void* stream) {
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows < 0");
+  if (K <= 0 || K % 128 != 0) return fail(MOE_ERR_INVALID_ARG, "K must be a positive multiple of 128");
+  if (scale_stride < K / 128) return fail(MOE_ERR_INVALID_ARG, "scale_stride < K/128");
+  if (rows == 0) return MOE_OK;
+  if (!in || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+  if (!aligned16(in) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "in must be 16-byte and codes 8-byte aligned");
+  QuantArgs q{};
+  q.rows = rows;
+  q.K = K;
+  q.in = in;
+  q.codes = codes;
+  q.scales = scales;
+  q.sstride = scale_stride;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(K_QUANT, s, [&] { return launch_quantize_fp8(q, s); });
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "quantize launch");
 }
 
 moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, const int32_t* slot_row,
@@ -574,6 +673,19 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
                       expert_counts, logits_out, ws, ws_bytes, static_cast<hipStream_t>(stream), nullptr);
 }
 
+moe_status moe_forward_fp8(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                           const float* logit_bias, const float* sel_bias, const uint8_t* w_gate, const uint8_t* s_gate,
+                           const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                           void* out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts, float* logits_out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  const moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  const Fp8Scales f8{s_gate, s_up, s_down};
+  return forward_impl(d, x, w_router, logit_bias, sel_bias, w_gate, w_up, w_down, out, topk_idx, topk_w,
+                      expert_counts, logits_out, ws, ws_bytes, static_cast<hipStream_t>(stream), nullptr, &f8);
+}
+
 moe_status moe_route_hash(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
                           const float* logit_bias, const float* logits_in, float* logits_out, const int32_t* token_ids,
                           const int32_t* tid2eid, int64_t vocab, int32_t* topk_idx, float* topk_w,
@@ -589,7 +701,7 @@ moe_status moe_route_hash(const moe_config* cfg, int64_t T, const void* x, const
     return fail(MOE_ERR_INVALID_ARG, "x and w_router must be 16-byte aligned");
   if (!topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "topk_idx and topk_w are required");
   Layout L{};
-  if (!logits_in && d.dtype == MOE_BF16) {
+  if (!logits_in && d.xdt == MOE_BF16) {
     st = check_ws(d, ws, ws_bytes, L);
     if (st != MOE_OK) return st;
   }

@@ -1,0 +1,423 @@
+// FP8 grouped expert GEMMs for gfx950: E4M3 operands with UE8M0 block scales
+// ("15. DeepSeek：MLA、MoE 与 MTP", section "FP8 训练是训练配方，不是架构": E4M3
+// inputs of the matrix products, one scale per 1 x 128 activation tile and
+// per 128 x 128 weight block; UE8M0 scales as in V3.1), and the 1 x 128 tile
+// quantisation of activations.
+//
+// The scales are applied inside the matrix cores: v_mfma_scale_f32_32x32x64
+// multiplies each operand's 32-element K block by 2^(s - 127) of its own
+// scale byte.  A 128-byte LDS tile row is one 128-wide K block, so every
+// MFMA of a K step uses one A scale per row and one B scale per weight block;
+// they are loaded one step ahead into registers.
+//
+// The tiling, LDS layout, XCD-aware work order and copy pipeline follow the
+// bf16 kernel (gemm.hip): 256-row x 256-column items, 4 wavefronts of
+// 128 x 128, two A stages and three B stages of 32 KB, XOR-swizzled rows.  A
+// K step (128 bytes) is two 64-wide sub-steps of v_mfma_scale_f32_32x32x64
+// (64 cycles each, the time of four bf16 sub-steps): the fragments of the
+// next sub-step are read under the current one's MFMAs, the single barrier
+// sits before the second sub-step, and the 16 copies of a step go out eight
+// per sub-step (A of step kt+1's second half and B of step kt+2's first
+// half, then B of step kt+2's second half and A of step kt+2's first half).
+//
+// The gate/up epilogue applies SwiGLU and quantises h per row and 128-wide
+// column block (one item covers exactly one such block): the row maximum is
+// reduced over the 32 lanes holding the row in each of the two wavefronts
+// that share it, exchanged through LDS, and turned into the UE8M0 exponent.
+#include "common.hpp"
+#include "gemm_sched.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowBytes = 128;         // one K step: 128 E4M3 values = one scale block
+constexpr int kBNB = 256;              // B rows per block tile
+constexpr int kWM = 128;               // rows per wavefront of a full tile
+constexpr int kAStage = 2 * kWM * kRowBytes;
+constexpr int kBStage = kBNB * kRowBytes;
+constexpr int kAStages = 2, kBStages = 3;
+constexpr int kLdsBytes = kAStages * kAStage + kBStages * kBStage;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
+
+// Exponent p of the UE8M0 scale of a tile whose largest magnitude is amax:
+// the smallest p >= -127 with amax / 2^p <= 448 (= 1.75 * 2^8); a zero or
+// subnormal maximum takes p = -127.
+__device__ __forceinline__ int e8m0_exp_of_amax(float amax) {
+  const uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
+  if (u < 0x00800000u) return -127;
+  const int E = (int)(u >> 23) - 127;
+  const int p = E - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return p < -127 ? -127 : p;
+}
+
+// E4M3 codes of two fp32 values (nearest-even, sign kept), in the low
+// 16 bits.
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Copies I0 .. I0+N-1 of a wave's group: copy i reads base + off[i] (bytes)
+// and fills the 1 KB of LDS at dst + i*1024.
+template <int I0, int N, int M>
+__device__ __forceinline__ void copy_rows8(const uint8_t* base, const uint32_t (&off)[M], char* dst) {
+  static_assert(I0 + N <= M, "copy range");
+#pragma unroll
+  for (int i = I0; i < I0 + N; ++i) copy16(reinterpret_cast<const bf16*>(base + off[i]), dst + i * 1024);
+}
+
+// Fragments of one 64-wide sub-step: lane half hf of row r takes the 16-byte
+// chunks 4s + hf and 4s + 2 + hf of the row (the MFMA's K order: bytes 0-15
+// of the operand are K 32j + 16hf + i of the block's first 32, bytes 16-31
+// the second 32).  slot0/slot1 are the swizzled byte offsets of the two chunks.
+template <int MB>
+__device__ __forceinline__ void load_frags8(const char* sa, const char* sb, int arow, const int (&brow)[4], int slot0,
+                                            int slot1, i32x8 (&fa)[MB], i32x8 (&fb)[4]) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const char* p = sa + arow + m * 32 * kRowBytes;
+    fa[m] = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(p + slot0),
+                                    *reinterpret_cast<const i32x4*>(p + slot1), 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const char* p = sb + brow[n];
+    fb[n] = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(p + slot0),
+                                    *reinterpret_cast<const i32x4*>(p + slot1), 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// One 64-wide sub-step of MFMAs with the current step's scales: sa[m] for
+// the lane's A row of block m, sb[n] for B block n.
+template <int MB>
+__device__ __forceinline__ void mfma_step8(const i32x8 (&fa)[MB], const i32x8 (&fb)[4], const int (&sa)[MB],
+                                           const int (&sb)[4], f32x16 (&acc)[MB][4]) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 0, sa[m], 0, sb[n]);
+}
+
+// Interleave one sub-step: two fragment reads after each of the first MB+4
+// MFMAs, then the NC copies one per MFMA (reads are written before copies in
+// program order, which the compiler keeps for LDS reads and LDS copies).
+template <int MB, int NC>
+__device__ __forceinline__ void interleave8() {
+  constexpr int NR = MB + 4, NM = MB * 4 - NR;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+  }
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 copy
+  }
+  if (NM > NC) __builtin_amdgcn_sched_group_barrier(0x008, NM - NC, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scales of K step kt: the lane's A rows (MB of them) and the wave's B blocks.
+template <int MB, bool GATEUP>
+__device__ __forceinline__ void load_scales(const GemmArgs& a, const int (&sidx)[MB], int64_t bidx0, int64_t bidx1,
+                                            int kt, int (&sa)[MB], int (&sb)[4]) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m) sa[m] = a.sa[sidx[m] + kt];
+  if constexpr (GATEUP) {
+    const int g = a.sb0[bidx0 + kt], u = a.sb1[bidx1 + kt];
+    sb[0] = g;
+    sb[1] = g;
+    sb[2] = u;
+    sb[3] = u;
+  } else {
+    const int d = a.sb0[bidx0 + kt];
+    sb[0] = d;
+    sb[1] = d;
+    sb[2] = d;
+    sb[3] = d;
+  }
+}
+
+template <int WM, bool GATEUP>
+__device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int e, int nt, int row0, int rows) {
+  constexpr int BM = 2 * WM;
+  constexpr int MB = WM / 32;
+  constexpr int A_PER_WAVE = BM / 8 / 4;
+  constexpr int B_PER_WAVE = kBNB / 8 / 4;
+  constexpr int AH = A_PER_WAVE / 2, BH = B_PER_WAVE / 2;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int K = a.K;  // bytes per row = E4M3 values per row
+  const int nk = K / kRowBytes;
+  const int lrow = lane >> 3;
+  const int wr = wave & 1, wc = wave >> 1;
+
+  const uint8_t* abase;
+  uint32_t aoff[A_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < A_PER_WAVE; ++i) {
+    const int r = (wave * A_PER_WAVE + i) * 8 + lrow;
+    const int rr = min(r, rows - 1);
+    const int chunk = (lane & 7) ^ swz_of_row(r);
+    if constexpr (GATEUP)
+      aoff[i] = (uint32_t)a.row_token[row0 + rr] * (uint32_t)K + chunk * 16;
+    else
+      aoff[i] = (uint32_t)rr * (uint32_t)K + chunk * 16;
+  }
+  if constexpr (GATEUP)
+    abase = static_cast<const uint8_t*>(a.a);
+  else
+    abase = static_cast<const uint8_t*>(a.a) + (int64_t)row0 * K;
+
+  const uint8_t* bbase;
+  uint32_t boff[B_PER_WAVE];
+  int64_t bidx0, bidx1;  // scale index of the wave's B block(s) at step 0
+  const int nkb = K / 128, nnb = a.N / 128;
+  if constexpr (GATEUP) {
+    bbase = static_cast<const uint8_t*>(wave < 2 ? a.b0 : a.b1) + ((int64_t)e * a.N + nt * 128) * K;
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int rb = ((wave & 1) * B_PER_WAVE + i) * 8 + lrow;
+      boff[i] = (uint32_t)rb * (uint32_t)K + ((lane & 7) ^ swz_of_row(rb)) * 16;
+    }
+    bidx0 = bidx1 = ((int64_t)e * nnb + nt) * nkb;
+  } else {
+    bbase = static_cast<const uint8_t*>(a.b0) + ((int64_t)e * a.N + nt * kBNB) * K;
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int rb = (wave * B_PER_WAVE + i) * 8 + lrow;
+      boff[i] = (uint32_t)rb * (uint32_t)K + ((lane & 7) ^ swz_of_row(rb)) * 16;
+    }
+    bidx0 = bidx1 = ((int64_t)e * nnb + nt * 2 + wc) * nkb;
+  }
+  // A scale rows of the lane: fragment m holds row wr*WM + m*32 + lane%32
+  int sidx[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int rr = min(wr * WM + m * 32 + (lane & 31), rows - 1);
+    if constexpr (GATEUP)
+      sidx[m] = a.row_token[row0 + rr] * a.sa_stride;
+    else
+      sidx[m] = (row0 + rr) * a.sa_stride;
+  }
+
+  char* const b_lds = lds + kAStages * kAStage;
+  char* const a_dst = lds + wave * A_PER_WAVE * 1024;
+  char* const b_dst = b_lds + wave * B_PER_WAVE * 1024;
+
+  f32x16 acc[MB][4];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+
+  const int arow = (wr * WM + (lane & 31)) * kRowBytes;
+  int brow[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    if constexpr (GATEUP)
+      brow[n] = ((n < 2 ? wc * 64 + n * 32 : 128 + wc * 64 + (n - 2) * 32) + (lane & 31)) * kRowBytes;
+    else
+      brow[n] = (wc * 128 + n * 32 + (lane & 31)) * kRowBytes;
+  }
+  const int hf = lane >> 5, sw = swz_of_row(lane & 15);
+  const int s00 = ((0 + hf) ^ sw) << 4, s01 = ((2 + hf) ^ sw) << 4;  // sub-step 0
+  const int s10 = ((4 + hf) ^ sw) << 4, s11 = ((6 + hf) ^ sw) << 4;  // sub-step 1
+
+  int sa_cur[MB], sb_cur[4], sa_nxt[MB], sb_nxt[4];
+  load_scales<MB, GATEUP>(a, sidx, bidx0, bidx1, 0, sa_cur, sb_cur);
+  // prologue: A of step 0 and half of step 1, B of steps 0 and 1
+  const uint8_t* const a1 = abase + min(1, nk - 1) * kRowBytes;
+  copy_rows8<0, A_PER_WAVE>(abase, aoff, a_dst);
+  copy_rows8<0, B_PER_WAVE>(bbase, boff, b_dst);
+  copy_rows8<0, AH>(a1, aoff, a_dst + kAStage);
+  copy_rows8<0, B_PER_WAVE>(bbase + min(1, nk - 1) * kRowBytes, boff, b_dst + kBStage);
+  wait_vmem_upto<AH + B_PER_WAVE>();
+  __builtin_amdgcn_s_barrier();
+
+  i32x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
+  int sbi = 0;
+  load_frags8<MB>(lds, b_lds, arow, brow, s00, s01, fa0, fb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* sa = lds + (kt & 1) * kAStage;
+    const char* sb = b_lds + sbi * kBStage;
+    const int sbn = sbi == kBStages - 1 ? 0 : sbi + 1;
+    const int sbf = sbn == kBStages - 1 ? 0 : sbn + 1;
+    const uint8_t* const an = abase + min(kt + 1, nk - 1) * kRowBytes;
+    const uint8_t* const bn = bbase + min(kt + 2, nk - 1) * kRowBytes;
+    // sub-step 0: scales of step kt+1, second half of A of step kt+1, first
+    // half of B of step kt+2
+    load_scales<MB, GATEUP>(a, sidx, bidx0, bidx1, min(kt + 1, nk - 1), sa_nxt, sb_nxt);
+    load_frags8<MB>(sa, sb, arow, brow, s10, s11, fa1, fb1);
+    copy_rows8<AH, A_PER_WAVE - AH>(an, aoff, a_dst + ((kt + 1) & 1) * kAStage);
+    copy_rows8<0, BH>(bn, boff, b_dst + sbf * kBStage);
+    mfma_step8<MB>(fa0, fb0, sa_cur, sb_cur, acc);
+    interleave8<MB, A_PER_WAVE - AH + BH>();
+    // the wave's reads of the current stages are done and A and B of step
+    // kt+1 have landed (only B of step kt+2's first half was issued after
+    // them); after the barrier every wave is past the current stages
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    wait_vmem_upto<BH>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1: step kt+1's first fragments, the rest of B of step kt+2
+    // and the first half of A of step kt+2 into the freed A stage
+    load_frags8<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, s00, s01, fa0, fb0);
+    copy_rows8<BH, B_PER_WAVE - BH>(bn, boff, b_dst + sbf * kBStage);
+    copy_rows8<0, AH>(abase + min(kt + 2, nk - 1) * kRowBytes, aoff, a_dst + (kt & 1) * kAStage);
+    mfma_step8<MB>(fa1, fb1, sa_cur, sb_cur, acc);
+    interleave8<MB, B_PER_WAVE - BH + AH>();
+#pragma unroll
+    for (int m = 0; m < MB; ++m) sa_cur[m] = sa_nxt[m];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) sb_cur[n] = sb_nxt[n];
+    sbi = sbn;
+  }
+  wait_vmem_upto<0>();
+
+  if constexpr (GATEUP) {
+    // SwiGLU, then E4M3 codes per row and 128-column block (this item's nt)
+    float amax[MB][16];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const float g = acc[m][n][r], u = acc[m][n + 2][r];
+          acc[m][n][r] = g / (1.0f + __expf(-g)) * u;
+        }
+        float v = fmaxf(__builtin_fabsf(acc[m][0][r]), __builtin_fabsf(acc[m][1][r]));
+        // over the 32 lanes of this half-wave (columns of the wave's 64)
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+        amax[m][r] = v;
+      }
+    // exchange with the wave holding the other 64 columns of the same rows
+    float* xch = reinterpret_cast<float*>(lds);  // [BM rows][2]
+    __syncthreads();                             // every wave is done with the stages
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wr * WM + m * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          xch[row * 2 + wc] = amax[m][r];
+        }
+    }
+    __syncthreads();
+    uint8_t* hq = static_cast<uint8_t*>(a.c);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr * WM + m * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (row >= rows) continue;
+        const float tile_max = fmaxf(amax[m][r], xch[row * 2 + (wc ^ 1)]);
+        const int p = e8m0_exp_of_amax(tile_max);
+        const uint32_t q = e4m3_pair(__builtin_amdgcn_ldexpf(acc[m][0][r], -p),
+                                     __builtin_amdgcn_ldexpf(acc[m][1][r], -p));
+        uint8_t* orow = hq + (int64_t)(row0 + row) * a.N + nt * 128 + wc * 64 + (lane & 31);
+        orow[0] = (uint8_t)(q & 0xFF);
+        orow[32] = (uint8_t)(q >> 8);
+        if (wc == 0 && (lane & 31) == 0) a.sc[(int64_t)(row0 + row) * a.sc_stride + nt] = (uint8_t)(p + 127);
+      }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr * WM + m * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (row >= rows) continue;
+        if (a.c16 == nullptr || e >= a.n_routed) {
+          const int64_t orow_i = (int64_t)(row0 + row) - (a.c16 ? a.routed_rows : 0);
+          float* orow = static_cast<float*>(a.c) + orow_i * a.N;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = acc[m][n][r];
+        } else {
+          bf16* orow = static_cast<bf16*>(a.c16) + (int64_t)(row0 + row) * a.N;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = (bf16)acc[m][n][r];
+        }
+      }
+    }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void expert_gemm_fp8(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  Work w;
+  if (!work_of_block(a, 2 * kWM, w)) return;
+  if (!w.pair) {
+    gemm_tile_fp8<kWM, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+  } else {
+    gemm_tile_fp8<kWM / 2, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+    if (w.nt + 1 < a.n_tiles) {
+      __syncthreads();
+      gemm_tile_fp8<kWM / 2, GATEUP>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+    }
+  }
+}
+
+// 1 x 128 tile quantisation: 16 lanes per tile, 8 values per lane.
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(QuantArgs a) {
+  const int tiles_per_row = a.K / 128;
+  const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (tile >= a.rows * tiles_per_row) return;
+  const int64_t row = tile / tiles_per_row;
+  const int tb = (int)(tile - row * tiles_per_row);
+  const int sub = threadIdx.x & 15;
+  const int64_t off = row * a.K + tb * 128 + sub * 8;
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.in) + off);
+  float f[8];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[i] = (float)v[i];
+    m = fmaxf(m, __builtin_fabsf(f[i]));
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const int p = e8m0_exp_of_amax(m);
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t lo = e4m3_pair(__builtin_amdgcn_ldexpf(f[4 * i], -p), __builtin_amdgcn_ldexpf(f[4 * i + 1], -p));
+    const uint32_t hi =
+        e4m3_pair(__builtin_amdgcn_ldexpf(f[4 * i + 2], -p), __builtin_amdgcn_ldexpf(f[4 * i + 3], -p));
+    w[i] = lo | (hi << 16);
+  }
+  *reinterpret_cast<uint2*>(a.codes + off) = make_uint2(w[0], w[1]);
+  if (sub == 0) a.scales[row * a.sstride + tb] = (uint8_t)(p + 127);
+}
+
+}  // namespace
+
+hipError_t launch_gateup_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s) {
+  const int64_t grid = mtile_bound * a.n_tiles;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((expert_gemm_fp8<true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s) {
+  const int64_t grid = mtile_bound * a.n_tiles;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((expert_gemm_fp8<false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t s) {
+  const int64_t tiles = a.rows * (a.K / 128);
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)((tiles + 15) / 16)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}

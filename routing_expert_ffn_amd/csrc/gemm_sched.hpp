@@ -1,0 +1,77 @@
+// Work items of the grouped expert GEMMs (shared by the bf16 and FP8 kernels):
+// the flat list of (expert, column tile, row tile) items built from the
+// device-side schedule, and its XCD-aware order.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kGroup = 4;             // full row tiles of an expert walked together
+
+// Work item of one workgroup.  The items of an expert are ordered as: groups
+// of up to kGroup full row tiles; inside a group, column-tile pairs (2p, 2p+1),
+// first every full row tile of the group at column 2p, then at 2p+1, then --
+// in the expert's last group only -- one item that runs the expert's short
+// last row tile (at most half_rows rows, half the MFMA work) at both columns.
+// Every item then takes about one full tile's time, items that share a weight
+// tile or a row tile of the input are close together, and each XCD (one L2)
+// walks a contiguous range of items, so neighbours run at the same time and
+// re-read shared operands from L2.
+struct Work {
+  int e, nt, row0, rows;
+  bool pair;  // short row tile at columns nt and nt + 1 (when nt + 1 exists)
+};
+
+__device__ __forceinline__ int items_before(const GemmArgs& a, int e, int np) {
+  return a.f_prefix[e] * a.n_tiles + a.h_prefix[e] * np;
+}
+
+__device__ __forceinline__ bool work_of_block(const GemmArgs& a, int BM, Work& w) {
+  const int ntn = a.n_tiles;
+  const int np = (ntn + 1) >> 1;
+  const int total = items_before(a, a.n_exp, np);
+  const int bid = blockIdx.x;
+  if (bid >= total) return false;
+  const int xcd = bid & 7, q = total >> 3, r = total & 7;
+  const int L = xcd * q + min(xcd, r) + (bid >> 3);
+  // largest e with items_before(e) <= L (experts without items are skipped)
+  int lo = 0, hi = a.n_exp;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (items_before(a, mid, np) <= L)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo;
+  int i = L - items_before(a, e, np);
+  const int F = a.f_prefix[e + 1] - a.f_prefix[e];
+  const int Hs = a.h_prefix[e + 1] - a.h_prefix[e];
+  const int nfg = max(1, (F + kGroup - 1) / kGroup);
+  const int g = min(i / (kGroup * ntn), nfg - 1);
+  i -= g * kGroup * ntn;
+  const int f = min(kGroup, F - g * kGroup);  // >= 1, or 0 when F == 0 (then Hs == 1)
+  const int h = g == nfg - 1 ? Hs : 0;
+  const int bs = 2 * f + h;                   // items per column pair
+  const int p = min(i / bs, np - 1);
+  const int j = i - p * bs;
+  const int ncols = 2 * p + 1 < ntn ? 2 : 1;
+  const int len = a.seg_len[e];
+  w.e = e;
+  if (j < f * ncols) {
+    const int mt = g * kGroup + j % f;
+    w.nt = 2 * p + j / f;
+    w.row0 = a.seg_start[e] + mt * BM;
+    w.rows = min(BM, len - mt * BM);
+    w.pair = false;
+  } else {
+    w.nt = 2 * p;
+    w.row0 = a.seg_start[e] + F * BM;
+    w.rows = len - F * BM;
+    w.pair = true;
+  }
+  return true;
+}
+
+}  // namespace

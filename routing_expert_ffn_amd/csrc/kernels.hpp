@@ -95,6 +95,25 @@ struct GemmArgs {
   // minus routed_rows; c16 == null: every row to c (fp32)
   void* c16;
   int n_routed, routed_rows;
+  // FP8 experts: a, b0, b1 and (gate/up) c hold E4M3 codes; UE8M0 scales of
+  // A per row and 128-wide K block, of B per 128 x 128 block, of h per row
+  // and 128-wide column block
+  const uint8_t* sa;        // gate/up: [T, sa_stride] (per token); down: [rows, sa_stride]
+  int sa_stride;
+  const uint8_t* sb0;       // [n_exp, N/128, K/128] scales of b0
+  const uint8_t* sb1;       // [n_exp, N/128, K/128] scales of b1 (gate/up)
+  uint8_t* sc;              // gate/up: [rows, sc_stride] scales of h
+  int sc_stride;
+};
+
+// 1 x 128 tile quantisation of bf16 rows to E4M3 codes and UE8M0 scales.
+struct QuantArgs {
+  int64_t rows;
+  int K;                    // multiple of 128
+  const void* in;           // [rows, K] bf16
+  uint8_t* codes;           // [rows, K]
+  uint8_t* scales;          // [rows, sstride]
+  int sstride;              // >= K/128
 };
 
 struct CombineArgs {
@@ -131,6 +150,7 @@ enum KernelId {
   K_DOWN,
   K_COMBINE,
   K_BALANCE,
+  K_QUANT,
   K_COUNT
 };
 
@@ -156,5 +176,10 @@ int gemm_bm(int dtype);
 int gemm_half_rows(int dtype);
 hipError_t launch_gateup(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStream_t s);
+// FP8 experts (gemm_fp8.hip): E4M3 operands with UE8M0 scales (GemmArgs sa,
+// sb0, sb1, sc), and the 1 x 128 quantisation of bf16 rows.
+hipError_t launch_gateup_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s);
+hipError_t launch_down_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s);
+hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t s);
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s);

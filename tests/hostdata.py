@@ -13,7 +13,7 @@ def to_oracle(t):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.numpy()
-    if t.dtype in (torch.int32, torch.int64):
+    if t.dtype in (torch.int32, torch.int64, torch.uint8):
         return t.numpy()
     raise TypeError(t.dtype)
 

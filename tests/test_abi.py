@@ -46,10 +46,12 @@ def test_workspace_sizes(name):
     s = CONFIGS[name]
     cfg = moe.make_config(s)
     n = moe.workspace_size(cfg, s.T)
-    esz = 2 if s.dtype == "bf16" else 4
+    hsz = {"fp8": 1, "bf16": 2, "f32": 4}[s.dtype]
     rows = s.T * s.k + s.S * s.T
-    # at least the SwiGLU activations and the expert rows
-    assert n >= rows * (s.I + s.H) * esz
+    # at least the SwiGLU activations (E4M3, bf16 or fp32) and the fp32 expert rows
+    assert n >= rows * (s.I * hsz + s.H * 4)
+    if s.dtype == "fp8":  # and x's E4M3 codes
+        assert n >= rows * (s.I + s.H * 4) + s.T * s.H
     assert n % 256 == 0
     assert moe.workspace_size(cfg, 0) < n
 

@@ -75,6 +75,13 @@ CONFIGS = {
                                          scoring=SQRTSOFTPLUS, renorm=True, scale=1.0, hash_vocab=129280,
                                          seed=707),
 }
+# The DeepSeek-V3-shaped layers with FP8 experts (E4M3 codes, 128 x 128 UE8M0
+# block scales; "15. DeepSeek：MLA、MoE 与 MTP", section on FP8 as a training
+# recipe): x and the router stay bf16.
+CONFIGS["deepseek_v3_prefill_fp8"] = CONFIGS["deepseek_v3_prefill"].with_(name="deepseek_v3_prefill_fp8", dtype="fp8",
+                                                                          seed=808)
+CONFIGS["deepseek_v3_decode_fp8"] = CONFIGS["deepseek_v3_decode"].with_(name="deepseek_v3_decode_fp8", dtype="fp8",
+                                                                        seed=909)
 
 # Reduced shapes with the same routing structure, small enough for the full
 # fp64 oracle to finish in seconds while still spanning several GEMM tiles and
@@ -88,6 +95,8 @@ TEST_SHAPES = {
     "v4_small": CONFIGS["deepseek_v4_flash"].with_(name="v4_small", T=517, H=512, I=256),
     "v4_hash_small": CONFIGS["deepseek_v4_flash_hash"].with_(name="v4_hash_small", T=389, H=512, I=256,
                                                              hash_vocab=3000),
+    "v3_fp8_small": CONFIGS["deepseek_v3_prefill_fp8"].with_(name="v3_fp8_small", T=517, H=512, I=384),
+    "v3_decode_fp8_small": CONFIGS["deepseek_v3_decode_fp8"].with_(name="v3_decode_fp8_small", H=512, I=256),
 }
 
 
