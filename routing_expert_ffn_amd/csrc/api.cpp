@@ -126,12 +126,17 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
 
 struct Layout {
   size_t logits, rpart, cand, idx, w, counts, offsets, slot_row, row_token, chunk_cnt, chunk_base, seg_start, seg_len,
-      f_prefix, h_prefix, h, y, xq, sx, sh, total;
+      f_prefix, h_prefix, h, y, xq, sx, sxr, sh, sbg, sbu, sbd, total;
 };
 
-// FP8 layers: row strides of the activation scale arrays (bytes)
+// bytes of a grouped row-space scale array (4-step groups of K/128 blocks)
+size_t grouped_scales(size_t rows, int nkb) { return ((size_t)(nkb + 3) / 4) * rows * 4; }
+int pad4(int n) { return (n + 3) & ~3; }
+
+// FP8 layers: x's tile scales per token ([T, H/128]); rows of the row space
+// (the K-block-major scale arrays of the GEMMs are [K/128, rows])
 int sx_stride(const Dims& d) { return d.H / 128; }
-int sh_stride(const Dims& d) { return d.I / 128; }
+int64_t row_space(const Dims& d) { return d.T * d.k + (int64_t)d.S * d.T; }
 
 Layout layout_of(const Dims& d) {
   Layout L{};
@@ -170,7 +175,13 @@ Layout layout_of(const Dims& d) {
   // FP8: x's codes and the scales of x and h
   L.xq = take(d.fp8 ? T * (size_t)d.H : 0);
   L.sx = take(d.fp8 ? T * (size_t)sx_stride(d) : 0);
-  L.sh = take(d.fp8 ? rows * (size_t)sh_stride(d) : 0);
+  L.sxr = take(d.fp8 ? grouped_scales(rows, d.H / 128) : 0);
+  L.sh = take(d.fp8 ? grouped_scales(rows, d.I / 128) : 0);
+  // weight block scales with rows padded to 4 bytes (used when the caller's
+  // rows are not already a multiple of 4 bytes)
+  L.sbg = take(d.fp8 ? (E + S) * (size_t)(d.I / 128) * pad4(d.H / 128) : 0);
+  L.sbu = take(d.fp8 ? (E + S) * (size_t)(d.I / 128) * pad4(d.H / 128) : 0);
+  L.sbd = take(d.fp8 ? (E + S) * (size_t)(d.H / 128) * pad4(d.I / 128) : 0);
   L.total = off;
   return L;
 }
@@ -387,6 +398,30 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
     q.sstride = sx_stride(d);
     e = timed(K_QUANT, s, [&] { return launch_quantize_fp8(q, s); });
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    RowScaleArgs r{};
+    r.n_rows = (int)row_space(d);
+    r.nkb = d.H / 128;
+    r.row_token = row_token;
+    r.sx = q.scales;
+    r.out = at<uint8_t>(ws, L.sxr);
+    e = timed(K_ROWSCALE, s, [&] { return launch_row_scales(r, s); });
+    if (e != hipSuccess) return hip_fail(e, "row scales launch");
+  }
+  Fp8Scales wsc{};  // weight scales as the GEMMs read them (rows of 4-byte multiples)
+  if (f8) {
+    auto usable = [](const uint8_t* p, int nkb) { return nkb % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (usable(f8->gate, d.H / 128) && usable(f8->up, d.H / 128) && usable(f8->down, d.I / 128)) {
+      wsc = *f8;
+    } else {
+      ScalePackArgs pk{};
+      const int64_t n_exp = d.E + d.S;
+      pk.m[0] = {n_exp * (d.I / 128), d.H / 128, f8->gate, at<uint8_t>(ws, L.sbg)};
+      pk.m[1] = {n_exp * (d.I / 128), d.H / 128, f8->up, at<uint8_t>(ws, L.sbu)};
+      pk.m[2] = {n_exp * (d.H / 128), d.I / 128, f8->down, at<uint8_t>(ws, L.sbd)};
+      e = timed(K_ROWSCALE, s, [&] { return launch_pack_scales(pk, s); });
+      if (e != hipSuccess) return hip_fail(e, "scale pack launch");
+      wsc = {pk.m[0].dst, pk.m[1].dst, pk.m[2].dst};
+    }
   }
   const int BM = gemm_bm(d.dtype);
   ScheduleArgs sa{};
@@ -422,12 +457,11 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   g.c = h;
   if (f8) {
     g.a = at<uint8_t>(ws, L.xq);
-    g.sa = at<uint8_t>(ws, L.sx);
-    g.sa_stride = sx_stride(d);
-    g.sb0 = f8->gate;
-    g.sb1 = f8->up;
+    g.sa = at<uint8_t>(ws, L.sxr);
+    g.n_rows = (int)row_space(d);
+    g.sb0 = wsc.gate;
+    g.sb1 = wsc.up;
     g.sc = at<uint8_t>(ws, L.sh);
-    g.sc_stride = sh_stride(d);
   }
   if (bound * g.n_tiles > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "too many GEMM tiles");
   e = timed(K_GATEUP, s, [&] { return launch_gateup(g, d.dtype, bound, s); });
@@ -441,8 +475,8 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   g.b1 = nullptr;
   if (f8) {
     g.sa = at<uint8_t>(ws, L.sh);
-    g.sa_stride = sh_stride(d);
-    g.sb0 = f8->down;
+    g.n_rows = (int)row_space(d);
+    g.sb0 = wsc.down;
     g.sb1 = nullptr;
     g.sc = nullptr;
   }
@@ -530,7 +564,7 @@ const char* kernel_name(int id) {
   static const char* names[K_COUNT] = {"fill",          "router",          "router_select", "capacity",
                                        "permute_count", "permute_scan",    "permute_scatter", "schedule",
                                        "gateup_swiglu", "down",            "combine",         "balance",
-                                       "quantize"};
+                                       "quantize",      "row_scales"};
   return (id >= 0 && id < K_COUNT) ? names[id] : nullptr;
 }
 

@@ -8,7 +8,9 @@
 // multiplies each operand's 32-element K block by 2^(s - 127) of its own
 // scale byte.  A 128-byte LDS tile row is one 128-wide K block, so every
 // MFMA of a K step uses one A scale per row and one B scale per weight block;
-// they are loaded one step ahead into registers.
+// they are loaded one step ahead into registers.  A's scales are stored
+// K-block-major over the row space, so the 32 rows of a fragment read 32
+// consecutive bytes (one request per load instead of one per row).
 //
 // The tiling, LDS layout, XCD-aware work order and copy pipeline follow the
 // bf16 kernel (gemm.hip): 256-row x 256-column items, 4 wavefronts of
@@ -24,6 +26,9 @@
 // column block (one item covers exactly one such block): the row maximum is
 // reduced over the 32 lanes holding the row in each of the two wavefronts
 // that share it, exchanged through LDS, and turned into the UE8M0 exponent.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemm_sched.hpp"
 #include "kernels.hpp"
@@ -101,12 +106,14 @@ __device__ __forceinline__ void mfma_step8(const i32x8 (&fa)[MB], const i32x8 (&
       acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 0, sa[m], 0, sb[n]);
 }
 
-// Interleave one sub-step: two fragment reads after each of the first MB+4
-// MFMAs, then the NC copies one per MFMA (reads are written before copies in
-// program order, which the compiler keeps for LDS reads and LDS copies).
-template <int MB, int NC>
+// Interleave one sub-step: NS scale loads first, two fragment reads after
+// each of the first MB+4 MFMAs, then the NC copies one per MFMA (reads are
+// written before copies in program order, which the compiler keeps for LDS
+// reads and LDS copies).
+template <int MB, int NC, int NS = 0>
 __device__ __forceinline__ void interleave8() {
   constexpr int NR = MB + 4, NM = MB * 4 - NR;
+  if (NS > 0) __builtin_amdgcn_sched_group_barrier(0x020, NS, 0);  // scale loads
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
@@ -121,25 +128,37 @@ __device__ __forceinline__ void interleave8() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Scales of K step kt: the lane's A rows (MB of them) and the wave's B blocks.
-template <int MB, bool GATEUP>
-__device__ __forceinline__ void load_scales(const GemmArgs& a, const int (&sidx)[MB], int64_t bidx0, int64_t bidx1,
-                                            int kt, int (&sa)[MB], int (&sb)[4]) {
+// An ordering point after which every accumulator has been produced.
+template <int MB>
+__device__ __forceinline__ void pin_acc(f32x16 (&acc)[MB][4]) {
 #pragma unroll
-  for (int m = 0; m < MB; ++m) sa[m] = a.sa[sidx[m] + kt];
-  if constexpr (GATEUP) {
-    const int g = a.sb0[bidx0 + kt], u = a.sb1[bidx1 + kt];
-    sb[0] = g;
-    sb[1] = g;
-    sb[2] = u;
-    sb[3] = u;
-  } else {
-    const int d = a.sb0[bidx0 + kt];
-    sb[0] = d;
-    sb[1] = d;
-    sb[2] = d;
-    sb[3] = d;
-  }
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) asm volatile("" ::"a"(acc[m][n]));
+}
+
+// Scales of the 4-step group g (steps 4g .. 4g+3, one per byte): one dword
+// per A row of the lane (grouped layout, see GemmArgs) and one uniform dword
+// per B block of the wave.
+template <int MB, bool GATEUP>
+__device__ __forceinline__ void load_scale_group(const GemmArgs& a, const int (&sidx)[MB], int64_t bw0, int64_t bw1,
+                                                 int g, uint32_t (&sa)[MB], uint32_t& sb0, uint32_t& sb1) {
+  const uint32_t* ag = reinterpret_cast<const uint32_t*>(a.sa) + (int64_t)g * a.n_rows;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) sa[m] = ag[sidx[m]];
+  sb0 = reinterpret_cast<const uint32_t*>(a.sb0)[bw0 + g];
+  sb1 = GATEUP ? reinterpret_cast<const uint32_t*>(a.sb1)[bw1 + g] : sb0;
+}
+
+// Scale operands of one step: byte `sh/8` of the group's dwords (the
+// instruction reads byte 0 of its scale operand).
+template <int MB>
+__device__ __forceinline__ void step_scales(const uint32_t (&ga)[MB], uint32_t gb0, uint32_t gb1, int sh, int (&sa)[MB],
+                                            int (&sb)[4]) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m) sa[m] = (int)(ga[m] >> sh);
+  sb[0] = sb[1] = (int)(gb0 >> sh);
+  sb[2] = sb[3] = (int)(gb1 >> sh);
 }
 
 template <int WM, bool GATEUP>
@@ -149,6 +168,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   constexpr int A_PER_WAVE = BM / 8 / 4;
   constexpr int B_PER_WAVE = kBNB / 8 / 4;
   constexpr int AH = A_PER_WAVE / 2, BH = B_PER_WAVE / 2;
+  constexpr int NSL = MB + (GATEUP ? 2 : 1);  // vector loads of one scale group
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -176,8 +196,9 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
 
   const uint8_t* bbase;
   uint32_t boff[B_PER_WAVE];
-  int64_t bidx0, bidx1;  // scale index of the wave's B block(s) at step 0
-  const int nkb = K / 128, nnb = a.N / 128;
+  int64_t bw0, bw1;  // dword index of the wave's B block(s) in the padded scale rows
+  const int nkb4 = ((K / 128) + 3) & ~3, nnb = a.N / 128;
+  const int ng = (nk + 3) >> 2;  // 4-step scale groups
   if constexpr (GATEUP) {
     bbase = static_cast<const uint8_t*>(wave < 2 ? a.b0 : a.b1) + ((int64_t)e * a.N + nt * 128) * K;
 #pragma unroll
@@ -185,7 +206,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
       const int rb = ((wave & 1) * B_PER_WAVE + i) * 8 + lrow;
       boff[i] = (uint32_t)rb * (uint32_t)K + ((lane & 7) ^ swz_of_row(rb)) * 16;
     }
-    bidx0 = bidx1 = ((int64_t)e * nnb + nt) * nkb;
+    bw0 = bw1 = ((int64_t)e * nnb + nt) * nkb4 / 4;
   } else {
     bbase = static_cast<const uint8_t*>(a.b0) + ((int64_t)e * a.N + nt * kBNB) * K;
 #pragma unroll
@@ -193,18 +214,12 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
       const int rb = (wave * B_PER_WAVE + i) * 8 + lrow;
       boff[i] = (uint32_t)rb * (uint32_t)K + ((lane & 7) ^ swz_of_row(rb)) * 16;
     }
-    bidx0 = bidx1 = ((int64_t)e * nnb + nt * 2 + wc) * nkb;
+    bw0 = bw1 = ((int64_t)e * nnb + nt * 2 + wc) * nkb4 / 4;
   }
   // A scale rows of the lane: fragment m holds row wr*WM + m*32 + lane%32
   int sidx[MB];
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int rr = min(wr * WM + m * 32 + (lane & 31), rows - 1);
-    if constexpr (GATEUP)
-      sidx[m] = a.row_token[row0 + rr] * a.sa_stride;
-    else
-      sidx[m] = (row0 + rr) * a.sa_stride;
-  }
+  for (int m = 0; m < MB; ++m) sidx[m] = row0 + min(wr * WM + m * 32 + (lane & 31), rows - 1);
 
   char* const b_lds = lds + kAStages * kAStage;
   char* const a_dst = lds + wave * A_PER_WAVE * 1024;
@@ -231,8 +246,8 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   const int s00 = ((0 + hf) ^ sw) << 4, s01 = ((2 + hf) ^ sw) << 4;  // sub-step 0
   const int s10 = ((4 + hf) ^ sw) << 4, s11 = ((6 + hf) ^ sw) << 4;  // sub-step 1
 
-  int sa_cur[MB], sb_cur[4], sa_nxt[MB], sb_nxt[4];
-  load_scales<MB, GATEUP>(a, sidx, bidx0, bidx1, 0, sa_cur, sb_cur);
+  uint32_t ga[MB], gb0, gb1, na[MB], nb0, nb1;  // scales of the current and the next group
+  load_scale_group<MB, GATEUP>(a, sidx, bw0, bw1, 0, ga, gb0, gb1);
   // prologue: A of step 0 and half of step 1, B of steps 0 and 1
   const uint8_t* const a1 = abase + min(1, nk - 1) * kRowBytes;
   copy_rows8<0, A_PER_WAVE>(abase, aoff, a_dst);
@@ -245,41 +260,72 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   i32x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
   int sbi = 0;
   load_frags8<MB>(lds, b_lds, arow, brow, s00, s01, fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // Scale groups: group g+1 is loaded at the start of sub-step 1 of step 4g
+  // (after that step's barrier) and becomes current after step 4g+3.  The
+  // steps of a group are written out (J = position in the group; the last
+  // steps when nk % 4 != 0 take J = -1 and test at run time), so these
+  // positions are fixed in the code: the loads are then forced complete by
+  // the barrier of step 4g+1 (one step of latency to hide), and the compiler
+  // sees them complete before their use instead of inserting a wait for every
+  // outstanding copy.
+  auto step = [&](int kt, auto J) {
+    constexpr int j = decltype(J)::value;
+    const bool first = j < 0 ? (kt & 3) == 0 : j == 0;
+    const bool last = j < 0 ? (kt & 3) == 3 : j == 3;
     const char* sa = lds + (kt & 1) * kAStage;
     const char* sb = b_lds + sbi * kBStage;
     const int sbn = sbi == kBStages - 1 ? 0 : sbi + 1;
     const int sbf = sbn == kBStages - 1 ? 0 : sbn + 1;
     const uint8_t* const an = abase + min(kt + 1, nk - 1) * kRowBytes;
     const uint8_t* const bn = bbase + min(kt + 2, nk - 1) * kRowBytes;
-    // sub-step 0: scales of step kt+1, second half of A of step kt+1, first
-    // half of B of step kt+2
-    load_scales<MB, GATEUP>(a, sidx, bidx0, bidx1, min(kt + 1, nk - 1), sa_nxt, sb_nxt);
+    int sa_k[MB], sb_k[4];
+    step_scales<MB>(ga, gb0, gb1, (kt & 3) * 8, sa_k, sb_k);
+    // sub-step 0: second half of A of step kt+1, first half of B of step kt+2
     load_frags8<MB>(sa, sb, arow, brow, s10, s11, fa1, fb1);
     copy_rows8<AH, A_PER_WAVE - AH>(an, aoff, a_dst + ((kt + 1) & 1) * kAStage);
     copy_rows8<0, BH>(bn, boff, b_dst + sbf * kBStage);
-    mfma_step8<MB>(fa0, fb0, sa_cur, sb_cur, acc);
+    mfma_step8<MB>(fa0, fb0, sa_k, sb_k, acc);
     interleave8<MB, A_PER_WAVE - AH + BH>();
     // the wave's reads of the current stages are done and A and B of step
     // kt+1 have landed (only B of step kt+2's first half was issued after
-    // them); after the barrier every wave is past the current stages
+    // them); after the barrier every wave is past the current stages.  (The
+    // empty asm statements consume the accumulators, so code placement cannot
+    // sink the sub-step's MFMAs past the barrier, where the matrix cores
+    // would sit idle while the wave waits.)
+    pin_acc<MB>(acc);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     wait_vmem_upto<BH>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // sub-step 1: step kt+1's first fragments, the rest of B of step kt+2
-    // and the first half of A of step kt+2 into the freed A stage
+    // sub-step 1: the next scale group (first step of a group), step kt+1's
+    // first fragments, the rest of B of step kt+2 and the first half of A of
+    // step kt+2 into the freed A stage
+    if (first) load_scale_group<MB, GATEUP>(a, sidx, bw0, bw1, min((kt >> 2) + 1, ng - 1), na, nb0, nb1);
     load_frags8<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, s00, s01, fa0, fb0);
     copy_rows8<BH, B_PER_WAVE - BH>(bn, boff, b_dst + sbf * kBStage);
     copy_rows8<0, AH>(abase + min(kt + 2, nk - 1) * kRowBytes, aoff, a_dst + (kt & 1) * kAStage);
-    mfma_step8<MB>(fa1, fb1, sa_cur, sb_cur, acc);
-    interleave8<MB, B_PER_WAVE - BH + AH>();
+    mfma_step8<MB>(fa1, fb1, sa_k, sb_k, acc);
+    if constexpr (j == 0)
+      interleave8<MB, B_PER_WAVE - BH + AH, NSL>();
+    else
+      interleave8<MB, B_PER_WAVE - BH + AH>();
+    pin_acc<MB>(acc);
+    if (last) {
 #pragma unroll
-    for (int m = 0; m < MB; ++m) sa_cur[m] = sa_nxt[m];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) sb_cur[n] = sb_nxt[n];
+      for (int m = 0; m < MB; ++m) ga[m] = na[m];
+      gb0 = nb0;
+      gb1 = nb1;
+    }
     sbi = sbn;
+  };
+  const int nfull = nk & ~3;
+  for (int kt = 0; kt < nfull; kt += 4) {
+    step(kt, std::integral_constant<int, 0>());
+    step(kt + 1, std::integral_constant<int, 1>());
+    step(kt + 2, std::integral_constant<int, 2>());
+    step(kt + 3, std::integral_constant<int, 3>());
   }
+  for (int kt = nfull; kt < nk; ++kt) step(kt, std::integral_constant<int, -1>());
   wait_vmem_upto<0>();
 
   if constexpr (GATEUP) {
@@ -327,7 +373,8 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
         uint8_t* orow = hq + (int64_t)(row0 + row) * a.N + nt * 128 + wc * 64 + (lane & 31);
         orow[0] = (uint8_t)(q & 0xFF);
         orow[32] = (uint8_t)(q >> 8);
-        if (wc == 0 && (lane & 31) == 0) a.sc[(int64_t)(row0 + row) * a.sc_stride + nt] = (uint8_t)(p + 127);
+        if (wc == 0 && (lane & 31) == 0)
+          a.sc[((int64_t)(nt >> 2) * a.n_rows + row0 + row) * 4 + (nt & 3)] = (uint8_t)(p + 127);
       }
   } else {
 #pragma unroll
@@ -399,7 +446,45 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(QuantArgs a) {
   if (sub == 0) a.scales[row * a.sstride + tb] = (uint8_t)(p + 127);
 }
 
+// Row-space copies of the tokens' x scales in the grouped layout:
+// out[((kb/4) * n_rows + r) * 4 + kb%4] = sx[row_token[r], kb] (unused rows
+// are skipped).
+__global__ __launch_bounds__(256) void row_scales_kernel(RowScaleArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.n_rows * a.nkb) return;
+  const int kb = (int)(i / a.n_rows), r = (int)(i - (int64_t)kb * a.n_rows);
+  const int t = a.row_token[r];
+  if (t >= 0) a.out[((int64_t)(kb >> 2) * a.n_rows + r) * 4 + (kb & 3)] = a.sx[(int64_t)t * a.nkb + kb];
+}
+
+// Weight block scales with rows padded to a multiple of 4 bytes (one
+// matrix per blockIdx.y): dst[row, kb] = src[row, kb], pad bytes 127.
+__global__ __launch_bounds__(256) void pack_scales_kernel(ScalePackArgs a) {
+  const ScalePackArgs::Mat& m = a.m[blockIdx.y];
+  const int nkb4 = (m.nkb + 3) & ~3;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)m.rows * nkb4) return;
+  const int64_t r = i / nkb4;
+  const int kb = (int)(i - r * nkb4);
+  m.dst[i] = kb < m.nkb ? m.src[r * m.nkb + kb] : (uint8_t)127;
+}
+
 }  // namespace
+
+hipError_t launch_pack_scales(const ScalePackArgs& a, hipStream_t s) {
+  int64_t n = 0;
+  for (int j = 0; j < 3; ++j) n = std::max<int64_t>(n, (int64_t)a.m[j].rows * ((a.m[j].nkb + 3) & ~3));
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)((n + 255) / 256), 3), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_scales(const RowScaleArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n_rows * a.nkb;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_scales_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gateup_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s) {
   const int64_t grid = mtile_bound * a.n_tiles;

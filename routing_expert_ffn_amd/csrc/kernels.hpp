@@ -96,14 +96,33 @@ struct GemmArgs {
   void* c16;
   int n_routed, routed_rows;
   // FP8 experts: a, b0, b1 and (gate/up) c hold E4M3 codes; UE8M0 scales of
-  // A per row and 128-wide K block, of B per 128 x 128 block, of h per row
-  // and 128-wide column block
-  const uint8_t* sa;        // gate/up: [T, sa_stride] (per token); down: [rows, sa_stride]
-  int sa_stride;
-  const uint8_t* sb0;       // [n_exp, N/128, K/128] scales of b0
-  const uint8_t* sb1;       // [n_exp, N/128, K/128] scales of b1 (gate/up)
-  uint8_t* sc;              // gate/up: [rows, sc_stride] scales of h
-  int sc_stride;
+  // A per row of the row space and 128-wide K block in the grouped layout
+  // [ceil(K/512), n_rows, 4] (byte kb%4 of row r's dword in group kb/4: one
+  // dword load brings four K steps, the rows of a tile are contiguous), of B
+  // per 128 x 128 block with rows padded to a multiple of 4 bytes, of h like A's
+  const uint8_t* sa;        // grouped [ceil(K/512), n_rows, 4]
+  int n_rows;               // rows of the row space (T*k + S*T)
+  const uint8_t* sb0;       // [n_exp, N/128, roundup(K/128, 4)] scales of b0, 4-byte aligned
+  const uint8_t* sb1;       // the same for b1 (gate/up)
+  uint8_t* sc;              // gate/up: grouped [ceil(N/512), n_rows, 4] scales of h
+};
+
+// Weight scales repacked with rows padded to 4 bytes (three matrices).
+struct ScalePackArgs {
+  struct Mat {
+    int64_t rows;           // n_exp * (N/128)
+    int nkb;                // K/128
+    const uint8_t* src;     // [rows, nkb]
+    uint8_t* dst;           // [rows, roundup(nkb, 4)]
+  } m[3];
+};
+
+// Per-row copies of the tokens' x scales for the FP8 gate/up GEMM.
+struct RowScaleArgs {
+  int n_rows, nkb;
+  const int32_t* row_token; // [n_rows], -1 = unused row
+  const uint8_t* sx;        // [T, nkb] per token
+  uint8_t* out;             // grouped [ceil(nkb/4), n_rows, 4]
 };
 
 // 1 x 128 tile quantisation of bf16 rows to E4M3 codes and UE8M0 scales.
@@ -151,6 +170,7 @@ enum KernelId {
   K_COMBINE,
   K_BALANCE,
   K_QUANT,
+  K_ROWSCALE,
   K_COUNT
 };
 
@@ -181,5 +201,7 @@ hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStr
 hipError_t launch_gateup_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s);
 hipError_t launch_down_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s);
 hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t s);
+hipError_t launch_row_scales(const RowScaleArgs& a, hipStream_t s);
+hipError_t launch_pack_scales(const ScalePackArgs& a, hipStream_t s);
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s);
