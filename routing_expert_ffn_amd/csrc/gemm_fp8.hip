@@ -23,9 +23,9 @@
 // half, then B of step kt+2's second half and A of step kt+2's first half).
 //
 // The gate/up epilogue applies SwiGLU and quantises h per row and 128-wide
-// column block (one item covers exactly one such block): the row maximum is
-// reduced over the 32 lanes holding the row in each of the two wavefronts
-// that share it, exchanged through LDS, and turned into the UE8M0 exponent.
+// column block (one item covers exactly one such block): h goes to an fp32
+// tile in LDS, then each thread takes one row, finds its maximum, turns it
+// into the UE8M0 exponent and writes the row's 128 codes.
 #include <algorithm>
 #include <type_traits>
 
@@ -329,53 +329,50 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   wait_vmem_upto<0>();
 
   if constexpr (GATEUP) {
-    // SwiGLU, then E4M3 codes per row and 128-column block (this item's nt)
-    float amax[MB][16];
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const float g = acc[m][n][r], u = acc[m][n + 2][r];
-          acc[m][n][r] = g / (1.0f + __expf(-g)) * u;
-        }
-        float v = fmaxf(__builtin_fabsf(acc[m][0][r]), __builtin_fabsf(acc[m][1][r]));
-        // over the 32 lanes of this half-wave (columns of the wave's 64)
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-        amax[m][r] = v;
-      }
-    // exchange with the wave holding the other 64 columns of the same rows
-    float* xch = reinterpret_cast<float*>(lds);  // [BM rows][2]
-    __syncthreads();                             // every wave is done with the stages
-    if ((lane & 31) == 0) {
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wr * WM + m * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          xch[row * 2 + wc] = amax[m][r];
-        }
-    }
-    __syncthreads();
-    uint8_t* hq = static_cast<uint8_t*>(a.c);
+    // SwiGLU into an fp32 tile in LDS (rows padded to 132 floats: a row's 16
+    // rows apart fall in distinct bank groups), then one thread per row: the
+    // row's maximum over its 128 columns (this item's 128-wide block of h),
+    // the UE8M0 scale, and the E4M3 codes written 16 bytes at a time
+    constexpr int kTS = 132;
+    float* tile = reinterpret_cast<float*>(lds);  // [BM][kTS]
+    __syncthreads();                              // every wave is done with the stages
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wr * WM + m * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (row >= rows) continue;
-        const float tile_max = fmaxf(amax[m][r], xch[row * 2 + (wc ^ 1)]);
-        const int p = e8m0_exp_of_amax(tile_max);
-        const uint32_t q = e4m3_pair(__builtin_amdgcn_ldexpf(acc[m][0][r], -p),
-                                     __builtin_amdgcn_ldexpf(acc[m][1][r], -p));
-        uint8_t* orow = hq + (int64_t)(row0 + row) * a.N + nt * 128 + wc * 64 + (lane & 31);
-        orow[0] = (uint8_t)(q & 0xFF);
-        orow[32] = (uint8_t)(q >> 8);
-        if (wc == 0 && (lane & 31) == 0)
-          a.sc[((int64_t)(nt >> 2) * a.n_rows + row0 + row) * 4 + (nt & 3)] = (uint8_t)(p + 127);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const float g = acc[m][n][r], u = acc[m][n + 2][r];
+          tile[row * kTS + wc * 64 + n * 32 + (lane & 31)] = g / (1.0f + __expf(-g)) * u;
+        }
       }
+    __syncthreads();
+    const int row = tid;
+    if (row < BM && row < rows) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(tile + row * kTS);
+      float mx = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const f32x4 v = src[c];
+        mx = fmaxf(mx, fmaxf(fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                             fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
+      }
+      const int p = e8m0_exp_of_amax(mx);
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.c) + (int64_t)(row0 + row) * a.N + nt * 128);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 v = src[c * 4 + i];
+          w[i] = e4m3_pair(__builtin_amdgcn_ldexpf(v[0], -p), __builtin_amdgcn_ldexpf(v[1], -p)) |
+                 (e4m3_pair(__builtin_amdgcn_ldexpf(v[2], -p), __builtin_amdgcn_ldexpf(v[3], -p)) << 16);
+        }
+        dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      a.sc[((int64_t)(nt >> 2) * a.n_rows + row0 + row) * 4 + (nt & 3)] = (uint8_t)(p + 127);
+    }
   } else {
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
