@@ -30,19 +30,21 @@ METRIC = "MoE-layer tokens/sec at DeepSeek-V3 shape; % bf16 MFMA peak / % HBM BW
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-GEMM_SRC = os.path.join(ROOT, "routing_expert_ffn_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "routing_expert_ffn_amd", "csrc")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gemm_source_sha():
-    with open(GEMM_SRC, "rb") as f:
+def gemm_source_sha(dtype):
+    """sha256[:16] of the source of the gate/up kernel of this dtype."""
+    name = "gemm_fp8.hip" if dtype == "fp8" else "gemm.hip"
+    with open(os.path.join(CSRC, name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, dtype):
     """HBM bytes per gate/up launch from the committed counter summary of
     this workload, or None when it is missing or was taken on another kernel
     source."""
@@ -52,7 +54,7 @@ def measured_traffic(workload):
     text = open(path).read()
     sha = re.search(r"gemm_source_sha:\s*([0-9a-f]+)", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not sha or not val or sha.group(1) != gemm_source_sha():
+    if not sha or not val or sha.group(1) != gemm_source_sha(dtype):
         return None
     return float(val.group(1))
 
@@ -215,7 +217,7 @@ def main():
                    "intermediate": shape.I, "scoring": shape.scoring, "capacity_factor": shape.capacity_factor,
                    "routing": "hash" if shape.hash_vocab else "learned", "out_dtype": "bf16"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": measured_traffic(shape.name),
+                     "frac": achieved / peak, "traffic": measured_traffic(shape.name, shape.dtype),
                      "kernel": "gateup_swiglu", "flops_per_launch": gateup_flops, "ms_per_launch": gu_ms},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
         "layer_mfma_frac": layer_flops / (ms_step * 1e-3) / 1e12 / peak,
