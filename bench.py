@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--workload", default="deepseek_v3_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--capacity-factor", type=float, default=None,
+                    help="override the workload's capacity factor (<= 0: unlimited)")
+    ap.add_argument("--drop-tokens", action="store_true", help="with a capacity: drop the overflow")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy 1 GiB device-to-device 3 times first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -131,6 +134,9 @@ def main():
     from workloads import CONFIGS, make_inputs
 
     shape = CONFIGS[args.workload]
+    if args.capacity_factor is not None or args.drop_tokens:
+        cf = shape.capacity_factor if args.capacity_factor is None else args.capacity_factor
+        shape = shape.with_(capacity_factor=cf, drop_tokens=args.drop_tokens)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log("generating inputs for", shape.name)
@@ -215,7 +221,8 @@ def main():
         "config": {"workload": shape.name, "tokens": T, "hidden": shape.H, "routed_experts": shape.E,
                    "shared_experts": shape.S, "top_k": shape.k, "groups": shape.G, "groups_kept": shape.topk_group,
                    "intermediate": shape.I, "scoring": shape.scoring, "capacity_factor": shape.capacity_factor,
-                   "routing": "hash" if shape.hash_vocab else "learned", "out_dtype": "bf16"},
+                   "drop_tokens": shape.drop_tokens, "routing": "hash" if shape.hash_vocab else "learned",
+                   "out_dtype": "bf16"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": measured_traffic(shape.name, shape.dtype),
                      "kernel": "gateup_swiglu", "flops_per_launch": gateup_flops, "ms_per_launch": gu_ms},

@@ -126,7 +126,7 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
 
 struct Layout {
   size_t logits, rpart, cand, idx, w, counts, offsets, slot_row, row_token, chunk_cnt, chunk_base, seg_start, seg_len,
-      f_prefix, h_prefix, h, y, xq, sx, sxr, sh, sbg, sbu, sbd, total;
+      f_prefix, h_prefix, h, y, xq, sx, sxr, sh, sbg, sbu, sbd, dcnt, total;
 };
 
 // bytes of a grouped row-space scale array (4-step groups of K/128 blocks)
@@ -170,6 +170,7 @@ Layout layout_of(const Dims& d) {
   L.seg_len = take((E + S) * 4);
   L.f_prefix = take((E + S + 1) * 4);
   L.h_prefix = take((E + S + 1) * 4);
+  L.dcnt = take(E * 4);  // drop mode: assignments per expert before the limit
   L.h = take(rows * (size_t)d.I * (d.fp8 ? 1 : d.esz));  // FP8: E4M3 codes of h
   L.y = take(rows * (size_t)d.H * 4);  // expert outputs are fp32
   // FP8: x's codes and the scales of x and h
@@ -300,15 +301,38 @@ moe_status do_route(const Dims& d, const void* x, const void* w_router, const fl
     }
     e = run_router(d, a, x, w_router, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "router kernel launch");
-    CapacityArgs c{};
-    c.p = route_params(d);
-    c.drop = 1;
-    c.cand = topk_idx;
-    c.topk_idx = topk_idx;
-    c.topk_w = topk_w;
-    c.counts = counts;
-    e = timed(K_CAPACITY, s, [&] { return launch_capacity(c, s); });
-    if (e != hipSuccess) return hip_fail(e, "capacity kernel launch");
+    // the permutation of the unlimited top-k gives every assignment its rank
+    // among its expert's assignments in token order; ranks >= C are dropped
+    PermuteArgs pa{};
+    pa.T = (int)d.T;
+    pa.E = d.E;
+    pa.k = d.k;
+    pa.S = d.S;
+    pa.nchunks = (int)((d.T + 63) / 64);
+    pa.topk_idx = topk_idx;
+    pa.chunk_cnt = at<int32_t>(ws, L.chunk_cnt);
+    pa.chunk_base = at<int32_t>(ws, L.chunk_base);
+    pa.counts = at<int32_t>(ws, L.dcnt);
+    pa.offsets = at<int32_t>(ws, L.offsets);
+    pa.row_token = at<int32_t>(ws, L.row_token);
+    pa.slot_row = at<int32_t>(ws, L.slot_row);
+    e = timed(K_PERM_COUNT, s, [&] { return launch_perm_count(pa, s); });
+    if (e == hipSuccess) e = timed(K_PERM_SCAN, s, [&] { return launch_perm_scan(pa, s); });
+    if (e == hipSuccess) e = timed(K_PERM_SCATTER, s, [&] { return launch_perm_scatter(pa, s); });
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    DropArgs dr{};
+    dr.T = (int)d.T;
+    dr.E = d.E;
+    dr.k = d.k;
+    dr.capacity = d.capacity;
+    dr.topk_idx = topk_idx;
+    dr.topk_w = topk_w;
+    dr.slot_row = pa.slot_row;
+    dr.offsets = pa.offsets;
+    dr.full_counts = pa.counts;
+    dr.counts = counts;
+    e = timed(K_CAPACITY, s, [&] { return launch_drop(dr, s); });
+    if (e != hipSuccess) return hip_fail(e, "drop kernel launch");
     return MOE_OK;
   }
   if (d.capacity > 0) {

@@ -45,8 +45,6 @@ struct RouterGemmArgs {
 
 struct CapacityArgs {
   RouteParams p;
-  int drop;                 // 1: cand is each token's top-k (= topk_idx); an
-                            // assignment to a full expert is dropped in place
   const float* logits;      // [T,E]
   const int32_t* cand;      // [T,n_allowed]
   int32_t* topk_idx;        // [T,k]
@@ -63,6 +61,19 @@ struct PermuteArgs {
   int32_t* offsets;         // [E+1]
   int32_t* row_token;       // [T*k + S*T]
   int32_t* slot_row;        // [T,k]
+};
+
+// Drop mode of the capacity limit: with the permutation of the unlimited
+// top-k, assignment (t, j) to expert e has rank slot_row - offsets[e] among
+// e's assignments in token order; ranks >= capacity are dropped.
+struct DropArgs {
+  int T, E, k, capacity;
+  int32_t* topk_idx;        // [T,k] in/out: dropped slots become -1
+  float* topk_w;            // [T,k] in/out: dropped slots get gate 0
+  const int32_t* slot_row;  // [T,k] rows of the unlimited permutation
+  const int32_t* offsets;   // [E+1]
+  const int32_t* full_counts; // [E] assignments before the limit
+  int32_t* counts;          // [E] out: min(full, capacity), or null
 };
 
 // Row segments of the experts (routed then shared) and the prefixes of their
@@ -188,6 +199,7 @@ hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s);
 hipError_t launch_perm_count(const PermuteArgs& a, hipStream_t s);
 hipError_t launch_perm_scan(const PermuteArgs& a, hipStream_t s);
 hipError_t launch_perm_scatter(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_drop(const DropArgs& a, hipStream_t s);
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
 // Upper bound of the m-tiles of all experts (grid sizing without a host sync).
 int64_t gemm_mtile_bound(int T, int E, int S, int k, int BM);

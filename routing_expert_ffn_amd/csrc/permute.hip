@@ -14,6 +14,8 @@
 //           chunk 0 stores them), row = offsets[e] + base[chunk][e] +
 //           popcount(mask[e] below the token's bit); no float atomics and
 //           no order dependence.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -135,6 +137,21 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(PermuteArgs a) {
   for (int s = 0; s < a.S; ++s) a.row_token[base + (int64_t)s * a.T + t] = t;
 }
 
+// Drop mode: an assignment whose rank in its expert's token-ordered rows is
+// at or beyond the capacity is dropped (first come, first served is then
+// exactly "keep while the expert holds fewer than C tokens").
+__global__ __launch_bounds__(256) void drop_kernel(DropArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (int64_t)a.T * a.k) {
+    const int e = a.topk_idx[i];
+    if (e >= 0 && e < a.E && a.slot_row[i] - a.offsets[e] >= a.capacity) {
+      a.topk_idx[i] = -1;
+      a.topk_w[i] = 0.0f;
+    }
+  }
+  if (a.counts && i < a.E) a.counts[i] = min(a.full_counts[i], a.capacity);
+}
+
 }  // namespace
 
 hipError_t launch_perm_count(const PermuteArgs& a, hipStream_t s) {
@@ -153,5 +170,12 @@ hipError_t launch_perm_scatter(const PermuteArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const size_t lds = sizeof(uint64_t) * a.E + sizeof(int32_t) * (a.E + 1);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(a.nchunks), dim3(64), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_drop(const DropArgs& a, hipStream_t s) {
+  const int64_t n = std::max<int64_t>((int64_t)a.T * a.k, a.E);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(drop_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -553,16 +553,15 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 // then serves the chunk's tokens in index order (lane r of a step looks at
 // rank base+r; candidates with room are taken in rank order until k are
 // chosen; counts live in LDS); all threads store the chunk's selections.
-// The gates follow in capacity_gates_kernel, one wavefront per token.  Drop
-// mode: the candidates are each token's top-k, slot j keeps its expert while
-// the expert has room and becomes -1 otherwise, and the top-k's gates stay.
+// The gates follow in capacity_gates_kernel, one wavefront per token.  (Drop
+// mode needs no serial pass: see drop_kernel in permute.hip.)
 constexpr int kCapWaves = 8;
 
 template <int NJ>
 __global__ __launch_bounds__(kCapWaves * 64) void capacity_kernel(CapacityArgs a, int chunk) {
   extern __shared__ int32_t lds_cap[];
   const RouteParams& p = a.p;
-  const int NA = a.drop ? p.k : p.n_allowed;
+  const int NA = p.n_allowed;
   int32_t* cnt = lds_cap;                   // [E]
   int32_t* cand = cnt + p.E;                // [chunk][NA]
   int32_t* sel = cand + chunk * NA;         // [chunk][k]
@@ -587,15 +586,6 @@ __global__ __launch_bounds__(kCapWaves * 64) void capacity_kernel(CapacityArgs a
           if (tt >= nt) break;
           const int32_t* c = cand + tt * NA;
           int32_t* s = sel + tt * p.k;
-          if (a.drop) {
-            // slot j keeps its expert while that expert has room (a token's
-            // experts are distinct: no two lanes count the same expert)
-            const int e = c0[i];
-            const bool room = e >= 0 && cnt[e] < p.capacity;
-            if (room) atomicAdd(&cnt[e], 1);
-            if (lane < p.k) s[lane] = room ? e : -1;
-            continue;
-          }
           int got = 0;
           for (int base = 0; base < NA && got < p.k; base += MOE_WAVE) {
             const int r = base + lane;
@@ -631,11 +621,6 @@ __global__ __launch_bounds__(256) void capacity_gates_kernel(CapacityArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
   const int my_e = lane < p.k ? a.topk_idx[(int64_t)t * p.k + lane] : -1;
-  if (a.drop) {
-    // the gates of the unlimited top-k stay; a dropped slot's gate is 0
-    if (lane < p.k && my_e < 0) a.topk_w[(int64_t)t * p.k + lane] = 0.0f;
-    return;
-  }
   const float g = token_gate<NJ>(p, a.logits + (int64_t)t * p.E, my_e, lane);
   if (lane < p.k) a.topk_w[(int64_t)t * p.k + lane] = my_e >= 0 ? g : 0.0f;
 }
@@ -680,7 +665,7 @@ template <int NJ>
 hipError_t launch_capacity_t(const CapacityArgs& a, hipStream_t s) {
   // chunk: candidates and selections of as many tokens as fit, with the
   // counts, in 64 KB of LDS (E <= 512, n_allowed <= E, k <= 32)
-  const int NA = a.drop ? a.p.k : a.p.n_allowed;
+  const int NA = a.p.n_allowed;
   const int chunk = std::max(1, std::min(a.p.T, 15360 / (NA + a.p.k)));
   const size_t lds = sizeof(int32_t) * ((size_t)a.p.E + (size_t)chunk * NA + (size_t)chunk * a.p.k);
   hipLaunchKernelGGL((capacity_kernel<NJ>), dim3(1), dim3(kCapWaves * 64), lds, s, a, chunk);

@@ -355,7 +355,8 @@ def test_hash_routing_drop_capacity_and_empty_table(cf):
     assert bool((idx == -1).all()) and bool((w == 0).all())
 
 
-@pytest.mark.parametrize("cf,drop", [(0.25, False), (1.25, False), (0.25, True), (1.25, True)])
+@pytest.mark.parametrize("cf,drop", [(0.25, False), (1.0, False), (1.2, False), (1.25, False), (0.25, True),
+                                     (1.0, True), (1.2, True), (1.25, True)])
 def test_capacity_with_drops_and_overflow(cf, drop):
     """Re-route mode (overflow to the next-best allowed expert) and drop mode
     (overflow assignments dropped, the top-k's gates kept)."""
