@@ -116,6 +116,44 @@ def test_route_needs_workspace_when_it_computes_bf16_logits():
     assert st == -3
 
 
+def test_variant_entry_points_validate_before_launch():
+    """Hash routing, FP8 and quantisation calls reject bad arguments on the
+    host (fake pointers are never dereferenced: validation fails first)."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(256 * 1024)
+    base = TEST_SHAPES["v3_small"]
+    # hash routing with a re-route capacity: no next-best expert exists
+    c = moe.make_config(base.with_(capacity_factor=1.0, drop_tokens=False))
+    st = L.moe_route_hash(ctypes.byref(c), 16, fake, fake, None, fake, None, fake, fake, 10, fake, fake, None, fake,
+                          1 << 40, None)
+    assert st == -1 and "drop_tokens" in L.moe_last_error().decode()
+    # negative vocabulary, missing token ids
+    c = moe.make_config(base)
+    assert L.moe_route_hash(ctypes.byref(c), 16, fake, fake, None, fake, None, fake, fake, -1, fake, fake, None,
+                            None, 0, None) == -1
+    assert L.moe_route_hash(ctypes.byref(c), 16, fake, fake, None, fake, None, None, fake, 10, fake, fake, None,
+                            None, 0, None) == -1
+    # FP8 entry points need dtype MOE_FP8, and MOE_FP8 layers need them
+    c = moe.make_config(base)
+    st = L.moe_forward_fp8(ctypes.byref(c), 16, fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake,
+                           None, None, None, None, fake, 1 << 40, None)
+    assert st == -1 and "MOE_FP8" in L.moe_last_error().decode()
+    c8 = moe.make_config(base.with_(dtype="fp8"))
+    st = L.moe_forward(ctypes.byref(c8), 16, fake, fake, None, None, fake, fake, fake, fake, None, None, None, None,
+                       fake, 1 << 40, None)
+    assert st == -1 and "moe_forward_fp8" in L.moe_last_error().decode()
+    st = L.moe_expert_ffn(ctypes.byref(c8), 16, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert st == -1
+    st = L.moe_forward_fp8(ctypes.byref(c8), 16, fake, fake, None, None, fake, None, fake, fake, fake, fake, fake,
+                           None, None, None, None, fake, 1 << 40, None)
+    assert st == -1 and "scale" in L.moe_last_error().decode()
+    # quantisation: K must be a multiple of 128, the scale stride cover K/128
+    assert L.moe_quantize_fp8(4, 100, fake, fake, fake, 1, None) == -1
+    assert L.moe_quantize_fp8(4, 256, fake, fake, fake, 1, None) == -1
+    assert L.moe_quantize_fp8(-1, 256, fake, fake, fake, 2, None) == -1
+    assert L.moe_quantize_fp8(0, 256, None, None, None, 2, None) == 0
+
+
 def test_empty_batch_is_a_noop():
     L = moe.lib()
     c = moe.make_config(TEST_SHAPES["v3_small"])
