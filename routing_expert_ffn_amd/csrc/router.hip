@@ -548,17 +548,16 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   }
 }
 
-// Capacity pass, one workgroup of kCapWaves wavefronts, tokens in chunks of
-// `chunk`: every thread copies the chunk's ranked candidates to LDS; wave 0
+// Capacity pass for small batches (a serial walk; cheaper than rounds when
+// experts fill about as often as tokens arrive), one workgroup of kCapWaves
+// wavefronts, tokens in chunks of `chunk`: every thread copies the chunk's ranked candidates to LDS; wave 0
 // then serves the chunk's tokens in index order (lane r of a step looks at
 // rank base+r; candidates with room are taken in rank order until k are
 // chosen; counts live in LDS); all threads store the chunk's selections.
-// The gates follow in capacity_gates_kernel, one wavefront per token.  (Drop
-// mode needs no serial pass: see drop_kernel in permute.hip.)
 constexpr int kCapWaves = 8;
 
 template <int NJ>
-__global__ __launch_bounds__(kCapWaves * 64) void capacity_kernel(CapacityArgs a, int chunk) {
+__global__ __launch_bounds__(kCapWaves * 64) void capacity_serial_kernel(CapacityArgs a, int chunk) {
   extern __shared__ int32_t lds_cap[];
   const RouteParams& p = a.p;
   const int NA = p.n_allowed;
@@ -613,6 +612,98 @@ __global__ __launch_bounds__(kCapWaves * 64) void capacity_kernel(CapacityArgs a
     for (int e = tid; e < p.E; e += kCapWaves * 64) a.counts[e] = cnt[e];
 }
 
+// Capacity pass (first come, first served in token order: each token takes
+// its best-ranked allowed experts that hold fewer than C tokens), one
+// workgroup, exact, in rounds over blocks of up to 64 tokens:
+//   1. every token of the block picks its first k candidates among the
+//      experts not full at the start of the round (8 lanes per token, the
+//      counts in LDS);
+//   2. per expert, a 64-bit mask of the block's tokens that picked it;
+//   3. a token's picks are final when each picked expert still has room
+//      after the block's earlier picks (count + popcount of the mask below
+//      the token < C): experts only fill, so its first k candidates among
+//      the experts with room at the round start are then exactly its first k
+//      among those with room when it is served.  The first token that fails
+//      (never the block's first) ends the round;
+//   4. the tokens before it are committed (counts += their picks) and the
+//      next round starts at it.
+// A round commits 64 tokens unless an expert fills inside the block, which
+// happens at most once per expert, so there are at most T/64 + E rounds.
+// The gates follow in capacity_gates_kernel, one wavefront per token.  (Drop
+// mode needs no pass at all: see drop_kernel in permute.hip.)
+constexpr int kCapThreads = 512;
+constexpr int kCapBlock = 64;
+
+template <int NJ>
+__global__ __launch_bounds__(kCapThreads) void capacity_kernel(CapacityArgs a) {
+  extern __shared__ int32_t lds_cap[];
+  const RouteParams& p = a.p;
+  const int E = p.E, k = p.k, NA = p.n_allowed, C = p.capacity;
+  int32_t* cnt = lds_cap;                                        // [E]
+  uint64_t* mask = reinterpret_cast<uint64_t*>(cnt + ((E + 1) & ~1));  // [E]
+  int32_t* tent = reinterpret_cast<int32_t*>(mask + E);          // [64][k]
+  int32_t* t_end = tent + kCapBlock * k;                          // [1]
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int e = tid; e < E; e += kCapThreads) {
+    cnt[e] = 0;
+    mask[e] = 0;
+  }
+  __syncthreads();
+  for (int t0 = 0; t0 < p.T;) {
+    const int nb = min(kCapBlock, p.T - t0);
+    // 1. picks among the experts with room at the round start
+    const int tt = tid >> 3, sub = tid & 7;
+    if (tt < nb) {
+      const int32_t* c = a.cand + (int64_t)(t0 + tt) * NA;
+      int got = 0;
+      for (int base = 0; got < k && base < NA; base += 8) {
+        const int r = base + sub;
+        const int e = r < NA ? c[r] : -1;
+        const bool room = e >= 0 && cnt[e] < C;
+        const uint32_t m8 = (uint32_t)(__ballot(room) >> (lane & ~7)) & 0xFFu;
+        const int need = k - got;
+        const int pre = __popc(m8 & ((1u << sub) - 1u));
+        if (room && pre < need) tent[tt * k + got + pre] = e;
+        got += min(__popc(m8), need);
+      }
+      for (int j = got + sub; j < k; j += 8) tent[tt * k + j] = -1;
+    }
+    __syncthreads();
+    // 2. per-expert masks of the block's picks
+    for (int i = tid; i < nb * k; i += kCapThreads) {
+      const int e = tent[i];
+      if (e >= 0) atomicOr((unsigned long long*)&mask[e], 1ull << (i / k));
+    }
+    __syncthreads();
+    // 3. the first token whose picks do not all still have room
+    if (tid < kCapBlock) {
+      bool bad = false;
+      if (tid < nb) {
+        const uint64_t below = (1ull << tid) - 1ull;
+        for (int j = 0; j < k; ++j) {
+          const int e = tent[tid * k + j];
+          if (e >= 0 && cnt[e] + __popcll(mask[e] & below) >= C) bad = true;
+        }
+      }
+      const uint64_t bm = __ballot(bad);
+      if (tid == 0) *t_end = bm ? __ffsll((long long)bm) - 1 : nb;
+    }
+    __syncthreads();
+    // 4. commit the tokens before it, clear the masks for the next round
+    const int ne = *t_end;
+    const uint64_t keep = ne >= 64 ? ~0ull : (1ull << ne) - 1ull;
+    for (int e = tid; e < E; e += kCapThreads) {
+      cnt[e] += __popcll(mask[e] & keep);
+      mask[e] = 0;
+    }
+    for (int i = tid; i < ne * k; i += kCapThreads) a.topk_idx[(int64_t)t0 * k + i] = tent[i];
+    t0 += ne;
+    __syncthreads();
+  }
+  if (a.counts)
+    for (int e = tid; e < E; e += kCapThreads) a.counts[e] = cnt[e];
+}
+
 // Gates of the final (capacity-limited) selection, one wavefront per token.
 template <int NJ>
 __global__ __launch_bounds__(256) void capacity_gates_kernel(CapacityArgs a) {
@@ -663,12 +754,21 @@ hipError_t launch_route_select_t(const RouterArgs& a, hipStream_t s) {
 
 template <int NJ>
 hipError_t launch_capacity_t(const CapacityArgs& a, hipStream_t s) {
-  // chunk: candidates and selections of as many tokens as fit, with the
-  // counts, in 64 KB of LDS (E <= 512, n_allowed <= E, k <= 32)
-  const int NA = a.p.n_allowed;
-  const int chunk = std::max(1, std::min(a.p.T, 15360 / (NA + a.p.k)));
-  const size_t lds = sizeof(int32_t) * ((size_t)a.p.E + (size_t)chunk * NA + (size_t)chunk * a.p.k);
-  hipLaunchKernelGGL((capacity_kernel<NJ>), dim3(1), dim3(kCapWaves * 64), lds, s, a, chunk);
+  if (a.p.T < 8 * a.p.E) {
+    // small batch: serial walk.  chunk: candidates and selections of as many
+    // tokens as fit, with the counts, in 64 KB of LDS (n_allowed <= E <= 512,
+    // k <= 32)
+    const int NA = a.p.n_allowed;
+    const int chunk = std::max(1, std::min(a.p.T, 15360 / (NA + a.p.k)));
+    const size_t lds = sizeof(int32_t) * ((size_t)a.p.E + (size_t)chunk * NA + (size_t)chunk * a.p.k);
+    hipLaunchKernelGGL((capacity_serial_kernel<NJ>), dim3(1), dim3(kCapWaves * 64), lds, s, a, chunk);
+  } else {
+    // rounds: counts, masks, the block's picks and the round's end (at most
+    // 14 KB)
+    const size_t lds = sizeof(int32_t) * (size_t)((a.p.E + 1) & ~1) + sizeof(uint64_t) * a.p.E +
+                       sizeof(int32_t) * ((size_t)kCapBlock * a.p.k + 1);
+    hipLaunchKernelGGL((capacity_kernel<NJ>), dim3(1), dim3(kCapThreads), lds, s, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((capacity_gates_kernel<NJ>), dim3((a.p.T + 3) / 4), dim3(256), 0, s, a);

@@ -23,7 +23,7 @@ import torch
 import oracle
 import routing_expert_ffn_amd as moe
 from tests.hostdata import to_oracle
-from workloads import CONFIGS, TEST_SHAPES, make_inputs
+from workloads import CONFIGS, TEST_SHAPES, make_inputs, zipf_logit_offsets
 
 pytestmark = pytest.mark.gpu
 
@@ -369,6 +369,30 @@ def test_capacity_with_drops_and_overflow(cf, drop):
     if cf < 1:
         assert (idx < 0).any()
     check_layer(shape, inp, g, np.arange(shape.T), "f32")
+
+
+@pytest.mark.parametrize("T,cf,G", [(2048, 1.0, 8), (5000, 1.25, 8), (16384, 1.25, 8), (16384, 0.5, 1),
+                                    (9000, 2.0, 8)])
+def test_capacity_rounds_match_oracle(T, cf, G):
+    """Large batches take the block-round capacity pass: bit-exact with the
+    oracle's serial first-come-first-served walk, on skewed logits where
+    experts fill inside blocks."""
+    E = 256
+    shape = TEST_SHAPES["v3_small"].with_(T=T, G=G, topk_group=4 if G > 1 else 1, capacity_factor=cf)
+    rng = np.random.default_rng(T + int(cf * 10))
+    skew = zipf_logit_offsets(E, 1.2, 7) * 2.0
+    L = (rng.standard_normal((T, E)) + skew).astype(np.float32)
+    sb = (rng.uniform(-0.05, 0.05, E)).astype(np.float32)
+    cfg = moe.make_config(shape)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    idx, w = moe.route(cfg, T, logits_in=torch.from_numpy(L).cuda(), sel_bias=torch.from_numpy(sb).cuda(),
+                       expert_counts=counts)
+    torch.cuda.synchronize()
+    oidx, ow, _, oc = oracle.select(shape, L, sb)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
+    assert oc.max() == oracle.capacity(shape, T) or cf >= 2.0
 
 
 def test_all_tokens_to_one_expert():
