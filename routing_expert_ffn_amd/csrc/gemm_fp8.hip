@@ -7,10 +7,11 @@
 // The scales are applied inside the matrix cores: v_mfma_scale_f32_32x32x64
 // multiplies each operand's 32-element K block by 2^(s - 127) of its own
 // scale byte.  A 128-byte LDS tile row is one 128-wide K block, so every
-// MFMA of a K step uses one A scale per row and one B scale per weight block;
-// they are loaded one step ahead into registers.  A's scales are stored
-// K-block-major over the row space, so the 32 rows of a fragment read 32
-// consecutive bytes (one request per load instead of one per row).
+// MFMA of a K step uses one A scale per row and one B scale per weight block.
+// Scales come in groups of four K steps (one dword per A row, one per B
+// block): A's in a row-space layout where a fragment's 32 rows are one
+// 128-byte line, B's in rows padded to four bytes; a group is loaded once
+// per four steps, a full step before the barrier that completes it.
 //
 // The tiling, LDS layout, XCD-aware work order and copy pipeline follow the
 // bf16 kernel (gemm.hip): 256-row x 256-column items, 4 wavefronts of
