@@ -2,9 +2,12 @@
 //   out[t] = sum_j w[t,j] * y_routed[slot_row[t,j]] + sum_s y_shared[s*T + t]
 // ("15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the
 // router sketch's last line: weighted routed experts plus the shared expert).
-// One workgroup per token; 16-byte loads of the expert rows (routed rows fp32
-// or bf16, shared rows fp32), fp32 accumulation in a fixed order (slots, then
-// shared experts), so the result is deterministic.
+// One workgroup per token (one thread per 8 values of the row); 16-byte loads
+// of the expert rows (routed rows fp32 or bf16, shared rows fp32), fp32
+// accumulation in a fixed order (slots, then shared experts), so the result
+// is deterministic.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -50,7 +53,7 @@ struct Vec8<float> {
 };
 
 template <typename TR, typename TO>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
   __shared__ int32_t srow[MOE_MAX_TOPK];
   __shared__ float sw[MOE_MAX_TOPK];
   const int t = blockIdx.x;
@@ -63,14 +66,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   TO* out = static_cast<TO*>(a.out) + (int64_t)t * a.H;
   for (int c = threadIdx.x * 8; c < a.H; c += blockDim.x * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // every slot loads (an empty slot reads row 0 and discards it), so the
+    // loads of all slots can be in flight together
     for (int j = 0; j < a.k; ++j) {
       const int r = srow[j];
-      if (r < 0) continue;
+      const bool live = r >= 0;
       const float w = sw[j];
       float v[8];
-      Vec8<TR>::load(y + (int64_t)r * a.H + c, v);
+      Vec8<TR>::load(y + (int64_t)(live ? r : 0) * a.H + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += w * v[i];
+      for (int i = 0; i < 8; ++i) acc[i] = live ? acc[i] + w * v[i] : acc[i];
     }
     for (int s = 0; s < a.S; ++s) {
       float v[8];
@@ -87,7 +92,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   (void)dtype;  // expert rows are fp32 for every input dtype
-  dim3 grid(a.T), block(256);
+  // one pass over the row: H/8 threads (a multiple of 64), at most 1024
+  const int threads = std::min(1024, std::max(64, ((a.H / 8 + 63) / 64) * 64));
+  dim3 grid(a.T), block(threads);
   if (a.routed_bf16 && out_dtype == 1)
     hipLaunchKernelGGL((combine_kernel<bf16, bf16>), grid, block, 0, s, a);
   else if (a.routed_bf16)
