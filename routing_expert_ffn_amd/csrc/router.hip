@@ -783,12 +783,14 @@ hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s) {
 }
 
 int router_splits(int64_t T, int H, int* sps) {
-  // enough (token tile, K slice) workgroups to cover the chip: 64-token
-  // tiles, K split into slices of whole 64-wide steps, at most 32 slices
+  // enough (token tile, K slice) workgroups for two per compute unit (80 KB
+  // of LDS each): the GEMM streams x from HBM with one step of prefetch, so
+  // its speed is the bytes in flight per CU; 64-token tiles, K split into
+  // slices of whole 64-wide steps, at most 32 slices
   const int nk = H / 64;
   const int64_t tiles = (T + 63) / 64;
   int S = 1;
-  if (tiles < 256) S = (int)std::min<int64_t>((256 + tiles - 1) / tiles, 32);
+  if (tiles < 512) S = (int)std::min<int64_t>((512 + tiles - 1) / tiles, 32);
   S = std::min(S, nk);
   const int per = (nk + S - 1) / S;
   *sps = per;
