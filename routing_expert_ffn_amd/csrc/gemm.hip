@@ -96,10 +96,11 @@ __device__ __forceinline__ void interleave_reads() {
 // sits before the last sub-step, once every wave has read its last fragments
 // of the current stages, so the matrix cores wait neither for the barrier nor
 // for the first LDS reads of the next step.  The copies refilling the freed
-// stages are spread over four sub-steps: half of A of step kt+2 in the last
-// sub-step of step kt, the other half in sub-step 0 of step kt+1, then B of
-// step kt+3 in its sub-steps 1 and 2 (B has three stages).  Before the
-// barrier of step kt a wave waits until only B of step kt+2 is in flight.
+// stages: B of step kt+2 in sub-steps 0 to 2 of step kt (B has three
+// stages, so its stage was freed by the previous barrier), A of step kt+2 in
+// the last sub-step, right after the barrier that frees its stage.  Before
+// the barrier of step kt a wave waits until only B of step kt+2 is in
+// flight, so every copy has at least a full step to land.
 
 // One output tile: rows [row0, row0 + rows) of expert e, column tile nt.  WM
 // is the row count per wavefront: kWM for a full tile (2*kWM rows), kWM/2 for
@@ -183,16 +184,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   for (int kk = 0; kk < 4; ++kk) slot[kk] = ((kk * 2 + (lane >> 5)) ^ swz_of_row(lane & 15)) << 4;
 
   const int nk = K / kBK;
-  constexpr int AH = A_PER_WAVE / 2, BH = B_PER_WAVE / 2;
-  // prologue: A of steps 0 and (half of) 1, B of steps 0 and 1 in flight
-  // (indices clamped to the last step: a re-copy lands in a stage that is not
-  // read again), then wait for step 0
-  const bf16* const a1 = abase + min(1, nk - 1) * kBK;
+  constexpr int BH = (B_PER_WAVE * 3 + 7) / 8, BH2 = 2 * BH;  // B copies in sub-steps 0 / 1 / 2
+  // prologue: A and B of steps 0 and 1 in the order of the main loop (B of a
+  // step before its A; indices clamped to the last step: a re-copy lands in
+  // a stage that is not read again), then wait for step 0
   copy_rows<0, A_PER_WAVE>(abase, aoff, a_dst);
   copy_rows<0, B_PER_WAVE>(bbase, boff, b_dst);
-  copy_rows<0, AH>(a1, aoff, a_dst + kAStage);
   copy_rows<0, B_PER_WAVE>(bbase + min(1, nk - 1) * kBK, boff, b_dst + kBStage);
-  wait_vmem_upto<AH + B_PER_WAVE>();
+  copy_rows<0, A_PER_WAVE>(abase + min(1, nk - 1) * kBK, aoff, a_dst + kAStage);
+  wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
   __builtin_amdgcn_s_barrier();
 
   bf16x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
@@ -203,22 +203,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
     const char* sb = b_lds + sbi * kBStage;
     const int sbn = sbi == kBStages - 1 ? 0 : sbi + 1;  // B stage of step kt+1
     const int sbf = sbn == kBStages - 1 ? 0 : sbn + 1;  // B stage of step kt+2 (free)
-    const bf16* const an = abase + min(kt + 1, nk - 1) * kBK;
     const bf16* const bn = bbase + min(kt + 2, nk - 1) * kBK;
-    // sub-step 0: second half of A of step kt+1
+    // sub-steps 0, 1 and 2: B of step kt+2 (3 + 3 + 2 copies) into the stage
+    // freed at the last barrier
     load_frags<MB>(sa, sb, arow, brow, slot[1], fa1, fb1);
-    copy_rows<AH, A_PER_WAVE - AH>(an, aoff, a_dst + ((kt + 1) & 1) * kAStage);
-    mfma_step<MB>(fa0, fb0, acc);
-    interleave_reads<MB, A_PER_WAVE - AH>();
-    // sub-steps 1 and 2: B of step kt+2
-    load_frags<MB>(sa, sb, arow, brow, slot[2], fa0, fb0);
     copy_rows<0, BH>(bn, boff, b_dst + sbf * kBStage);
+    mfma_step<MB>(fa0, fb0, acc);
+    interleave_reads<MB, BH>();
+    load_frags<MB>(sa, sb, arow, brow, slot[2], fa0, fb0);
+    copy_rows<BH, BH>(bn, boff, b_dst + sbf * kBStage);
     mfma_step<MB>(fa1, fb1, acc);
     interleave_reads<MB, BH>();
     load_frags<MB>(sa, sb, arow, brow, slot[3], fa1, fb1);
-    copy_rows<BH, B_PER_WAVE - BH>(bn, boff, b_dst + sbf * kBStage);
+    copy_rows<BH2, B_PER_WAVE - BH2>(bn, boff, b_dst + sbf * kBStage);
     mfma_step<MB>(fa0, fb0, acc);
-    interleave_reads<MB, B_PER_WAVE - BH>();
+    interleave_reads<MB, B_PER_WAVE - BH2>();
     // this wave's reads of the current stages are done and A and B of step
     // kt+1 have landed (copies complete in issue order; only B of step kt+2
     // was issued after them); after the barrier every wave is past the
@@ -227,13 +226,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
     wait_vmem_upto<B_PER_WAVE>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // last sub-step: first half of A of step kt+2 into the freed A stage and
-    // step kt+1's first fragments (after the last step: harmless reads of
-    // unused stages)
+    // last sub-step: A of step kt+2 into the A stage just freed, and step
+    // kt+1's first fragments (after the last step: harmless reads of unused
+    // stages).  Every copy thus has a full step or more before the barrier
+    // that needs it.
     load_frags<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, slot[0], fa0, fb0);
-    copy_rows<0, AH>(abase + min(kt + 2, nk - 1) * kBK, aoff, a_dst + (kt & 1) * kAStage);
+    copy_rows<0, A_PER_WAVE>(abase + min(kt + 2, nk - 1) * kBK, aoff, a_dst + (kt & 1) * kAStage);
     mfma_step<MB>(fa1, fb1, acc);
-    interleave_reads<MB, AH>();
+    interleave_reads<MB, A_PER_WAVE>();
     sbi = sbn;
   }
   // no copy may still be writing LDS when the stages are reused or released

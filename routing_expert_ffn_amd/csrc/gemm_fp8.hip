@@ -19,9 +19,12 @@
 // K step (128 bytes) is two 64-wide sub-steps of v_mfma_scale_f32_32x32x64
 // (64 cycles each, the time of four bf16 sub-steps): the fragments of the
 // next sub-step are read under the current one's MFMAs, the single barrier
-// sits before the second sub-step, and the 16 copies of a step go out eight
-// per sub-step (A of step kt+1's second half and B of step kt+2's first
-// half, then B of step kt+2's second half and A of step kt+2's first half).
+// sits before the second sub-step, and the copies of step kt go out as B of
+// step kt+2 in the first sub-step and A of step kt+2 in the second.  With
+// only two sub-steps per barrier, a copy issued after the barrier's half of
+// the step would have half a step to land; this order gives every copy at
+// least a full step, which is what sets the pace when the weights stream
+// from HBM with little MFMA work per step (small batches).
 //
 // The gate/up epilogue applies SwiGLU and quantises h per row and 128-wide
 // column block (one item covers exactly one such block): h goes to an fp32
@@ -168,7 +171,6 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   constexpr int MB = WM / 32;
   constexpr int A_PER_WAVE = BM / 8 / 4;
   constexpr int B_PER_WAVE = kBNB / 8 / 4;
-  constexpr int AH = A_PER_WAVE / 2, BH = B_PER_WAVE / 2;
   constexpr int NSL = MB + (GATEUP ? 2 : 1);  // vector loads of one scale group
 
   const int tid = threadIdx.x;
@@ -249,13 +251,13 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
 
   uint32_t ga[MB], gb0, gb1, na[MB], nb0, nb1;  // scales of the current and the next group
   load_scale_group<MB, GATEUP>(a, sidx, bw0, bw1, 0, ga, gb0, gb1);
-  // prologue: A of step 0 and half of step 1, B of steps 0 and 1
-  const uint8_t* const a1 = abase + min(1, nk - 1) * kRowBytes;
+  // prologue: A and B of steps 0 and 1 in the order of the main loop (B of a
+  // step before its A), then wait for step 0
   copy_rows8<0, A_PER_WAVE>(abase, aoff, a_dst);
   copy_rows8<0, B_PER_WAVE>(bbase, boff, b_dst);
-  copy_rows8<0, AH>(a1, aoff, a_dst + kAStage);
   copy_rows8<0, B_PER_WAVE>(bbase + min(1, nk - 1) * kRowBytes, boff, b_dst + kBStage);
-  wait_vmem_upto<AH + B_PER_WAVE>();
+  copy_rows8<0, A_PER_WAVE>(abase + min(1, nk - 1) * kRowBytes, aoff, a_dst + kAStage);
+  wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
   __builtin_amdgcn_s_barrier();
 
   i32x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
@@ -277,39 +279,37 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
     const char* sb = b_lds + sbi * kBStage;
     const int sbn = sbi == kBStages - 1 ? 0 : sbi + 1;
     const int sbf = sbn == kBStages - 1 ? 0 : sbn + 1;
-    const uint8_t* const an = abase + min(kt + 1, nk - 1) * kRowBytes;
-    const uint8_t* const bn = bbase + min(kt + 2, nk - 1) * kRowBytes;
     int sa_k[MB], sb_k[4];
     step_scales<MB>(ga, gb0, gb1, (kt & 3) * 8, sa_k, sb_k);
-    // sub-step 0: second half of A of step kt+1, first half of B of step kt+2
+    // sub-step 0: B of step kt+2 into the stage freed at the last barrier
     load_frags8<MB>(sa, sb, arow, brow, s10, s11, fa1, fb1);
-    copy_rows8<AH, A_PER_WAVE - AH>(an, aoff, a_dst + ((kt + 1) & 1) * kAStage);
-    copy_rows8<0, BH>(bn, boff, b_dst + sbf * kBStage);
+    copy_rows8<0, B_PER_WAVE>(bbase + min(kt + 2, nk - 1) * kRowBytes, boff, b_dst + sbf * kBStage);
     mfma_step8<MB>(fa0, fb0, sa_k, sb_k, acc);
-    interleave8<MB, A_PER_WAVE - AH + BH>();
+    interleave8<MB, B_PER_WAVE>();
     // the wave's reads of the current stages are done and A and B of step
-    // kt+1 have landed (only B of step kt+2's first half was issued after
-    // them); after the barrier every wave is past the current stages.  (The
-    // empty asm statements consume the accumulators, so code placement cannot
-    // sink the sub-step's MFMAs past the barrier, where the matrix cores
-    // would sit idle while the wave waits.)
+    // kt+1 have landed (only B of step kt+2 was issued after them); after the
+    // barrier every wave is past the current stages.  (The empty asm
+    // statements consume the accumulators, so code placement cannot sink the
+    // sub-step's MFMAs past the barrier, where the matrix cores would sit idle
+    // while the wave waits.)
     pin_acc<MB>(acc);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    wait_vmem_upto<BH>();
+    wait_vmem_upto<B_PER_WAVE>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // sub-step 1: the next scale group (first step of a group), step kt+1's
-    // first fragments, the rest of B of step kt+2 and the first half of A of
-    // step kt+2 into the freed A stage
+    // first fragments, and A of step kt+2 into the A stage just freed.  Every
+    // copy thus has a full step or more before the barrier that needs it:
+    // A from here to the next step's barrier, B from sub-step 0 to the
+    // barrier of the step after next.
     if (first) load_scale_group<MB, GATEUP>(a, sidx, bw0, bw1, min((kt >> 2) + 1, ng - 1), na, nb0, nb1);
     load_frags8<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, s00, s01, fa0, fb0);
-    copy_rows8<BH, B_PER_WAVE - BH>(bn, boff, b_dst + sbf * kBStage);
-    copy_rows8<0, AH>(abase + min(kt + 2, nk - 1) * kRowBytes, aoff, a_dst + (kt & 1) * kAStage);
+    copy_rows8<0, A_PER_WAVE>(abase + min(kt + 2, nk - 1) * kRowBytes, aoff, a_dst + (kt & 1) * kAStage);
     mfma_step8<MB>(fa1, fb1, sa_k, sb_k, acc);
     if constexpr (j == 0)
-      interleave8<MB, B_PER_WAVE - BH + AH, NSL>();
+      interleave8<MB, A_PER_WAVE, NSL>();
     else
-      interleave8<MB, B_PER_WAVE - BH + AH>();
+      interleave8<MB, A_PER_WAVE>();
     pin_acc<MB>(acc);
     if (last) {
 #pragma unroll
