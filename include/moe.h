@@ -46,6 +46,11 @@
  *    message for moe_last_error().  A failed kernel launch returns
  *    MOE_ERR_HIP.  Faults inside kernels surface asynchronously (at the
  *    caller's next synchronisation).  T == 0 is a successful no-op.
+ *  - Size limit of the expert FFN (moe_forward*, moe_expert_ffn*): for bf16
+ *    and FP8 layers x must hold fewer than 2^31 bytes (T * H * 2 for bf16,
+ *    T * H E4M3 codes for FP8), else MOE_ERR_UNSUPPORTED: the gate/up GEMM
+ *    gathers token rows through one 32-bit buffer resource.  Split larger
+ *    batches.
  *  - Routing is reproducible bit for bit: selection works on fp32 values with
  *    ties broken by the lower index, and sigmoid selection scores use the fp32
  *    sigmoid built from correctly rounded operations that moe_route documents.

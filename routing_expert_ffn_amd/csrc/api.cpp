@@ -194,6 +194,14 @@ P* at(void* ws, size_t off) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The bf16/FP8 gate/up GEMM gathers token rows through one buffer resource
+// over x (bf16) or its E4M3 codes (FP8), whose byte size must fit in 31 bits.
+moe_status check_gemm_x(const Dims& d) {
+  if (d.dtype != MOE_F32 && d.T * (int64_t)d.H * (d.fp8 ? 1 : 2) > 0x7FFFFFFF)
+    return fail(MOE_ERR_UNSUPPORTED, "T * hidden_size * element size must be below 2 GiB (x of bf16 and FP8 layers)");
+  return MOE_OK;
+}
+
 moe_status check_ws(const Dims& d, void* ws, size_t ws_bytes, Layout& L) {
   L = layout_of(d);
   if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
@@ -476,6 +484,7 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   g.N = d.I;
   g.n_tiles = d.dtype != MOE_F32 ? d.I / 128 : d.I / 32;
   g.a = x;
+  g.a_bytes = (uint32_t)(d.T * d.H * (f8 ? 1 : d.esz));
   g.b0 = w_gate;
   g.b1 = w_up;
   g.c = h;
@@ -549,6 +558,8 @@ moe_status forward_impl(const Dims& d, const void* x, const void* w_router, cons
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
       !aligned16(out))
     return fail(MOE_ERR_INVALID_ARG, "x, weights and out must be 16-byte aligned");
+  st = check_gemm_x(d);
+  if (st != MOE_OK) return st;
   Layout L{};
   st = check_ws(d, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
@@ -660,6 +671,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(y_rows))
     return fail(MOE_ERR_INVALID_ARG, "x, weights and y_rows must be 16-byte aligned");
   if (d.fp8) return fail(MOE_ERR_INVALID_ARG, "MOE_FP8 layers run through moe_expert_ffn_fp8");
+  st = check_gemm_x(d);
+  if (st != MOE_OK) return st;
   Layout L{};
   st = check_ws(d, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
@@ -679,6 +692,8 @@ moe_status moe_expert_ffn_fp8(const moe_config* cfg, int64_t T, const void* x, c
     return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(y_rows))
     return fail(MOE_ERR_INVALID_ARG, "x, weights and y_rows must be 16-byte aligned");
+  st = check_gemm_x(d);
+  if (st != MOE_OK) return st;
   Layout L{};
   st = check_ws(d, ws, ws_bytes, L);
   if (st != MOE_OK) return st;

@@ -109,3 +109,18 @@ __device__ __forceinline__ int swz_of_row(int r) { return (r & 7) ^ ((r >> 3) & 
 __device__ __forceinline__ void copy16(const bf16* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
 }
+
+// Raw buffer resource over [base, base + bytes), bytes < 2^31: a buffer load
+// whose offset lies past the end returns zeros and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Lane offset that is past the end of every resource made by raw_rsrc.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// The buffer form of copy16: lane L reads 16 bytes at voff + soff of the
+// resource (zeros when voff is out of range) into LDS bytes [dst + 16*L, +16).
+__device__ __forceinline__ void copy16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, soff, 0, 0);
+}

@@ -49,6 +49,16 @@ __device__ __forceinline__ void copy_rows(const bf16* base, const uint32_t (&off
   for (int i = I0; i < I0 + N; ++i) copy16(base + off[i], dst + i * 1024);
 }
 
+// The same through a buffer resource: copy i reads byte voff[i] + soff
+// (zeros for a row past the tile's end, whose offset is out of range).
+template <int I0, int N, int M>
+__device__ __forceinline__ void copy_rows_buf(__amdgpu_buffer_rsrc_t r, const uint32_t (&voff)[M], uint32_t soff,
+                                              char* dst) {
+  static_assert(I0 + N <= M, "copy range");
+#pragma unroll
+  for (int i = I0; i < I0 + N; ++i) copy16_buf(r, voff[i], soff, dst + i * 1024);
+}
+
 // MFMA operand fragments of one 16-wide K step from the swizzled LDS tiles
 // (sa: A stage, sb: B stage).
 template <int MB>
@@ -120,22 +130,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   // row L/8 of its group, slot L%8, so it fetches chunk (L%8) ^ sw(row)
   const int lrow = lane >> 3;
 
-  const bf16* abase;
+  // A rows through a buffer resource (byte offsets): the rows of the tile
+  // past `rows` read as zeros, so padding rows cost no memory traffic and
+  // feed zeros to the matrix cores
+  __amdgpu_buffer_rsrc_t arsrc;
   uint32_t aoff[A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < A_PER_WAVE; ++i) {
     const int r = (wave * A_PER_WAVE + i) * 8 + lrow;
-    const int rr = min(r, rows - 1);
-    const int chunk = (lane & 7) ^ swz_of_row(r);
+    const uint32_t chunk = (uint32_t)((lane & 7) ^ swz_of_row(r)) * 16u;
     if constexpr (GATEUP)
-      aoff[i] = (uint32_t)a.row_token[row0 + rr] * (uint32_t)K + chunk * 8;
+      aoff[i] = r < rows ? (uint32_t)a.row_token[row0 + r] * (uint32_t)(2 * K) + chunk : kOutOfRange;
     else
-      aoff[i] = (uint32_t)rr * (uint32_t)K + chunk * 8;
+      aoff[i] = r < rows ? (uint32_t)r * (uint32_t)(2 * K) + chunk : kOutOfRange;
   }
   if constexpr (GATEUP)
-    abase = static_cast<const bf16*>(a.a);
+    arsrc = raw_rsrc(a.a, a.a_bytes);
   else
-    abase = static_cast<const bf16*>(a.a) + (int64_t)row0 * K;
+    arsrc = raw_rsrc(static_cast<const bf16*>(a.a) + (int64_t)row0 * K, (uint32_t)rows * (uint32_t)(2 * K));
 
   const bf16* bbase;
   uint32_t boff[B_PER_WAVE];
@@ -188,10 +200,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   // prologue: A and B of steps 0 and 1 in the order of the main loop (B of a
   // step before its A; indices clamped to the last step: a re-copy lands in
   // a stage that is not read again), then wait for step 0
-  copy_rows<0, A_PER_WAVE>(abase, aoff, a_dst);
+  copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, 0, a_dst);
   copy_rows<0, B_PER_WAVE>(bbase, boff, b_dst);
   copy_rows<0, B_PER_WAVE>(bbase + min(1, nk - 1) * kBK, boff, b_dst + kBStage);
-  copy_rows<0, A_PER_WAVE>(abase + min(1, nk - 1) * kBK, aoff, a_dst + kAStage);
+  copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, min(1, nk - 1) * kRowBytes, a_dst + kAStage);
   wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
   __builtin_amdgcn_s_barrier();
 
@@ -231,7 +243,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
     // stages).  Every copy thus has a full step or more before the barrier
     // that needs it.
     load_frags<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, slot[0], fa0, fb0);
-    copy_rows<0, A_PER_WAVE>(abase + min(kt + 2, nk - 1) * kBK, aoff, a_dst + (kt & 1) * kAStage);
+    copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, min(kt + 2, nk - 1) * kRowBytes, a_dst + (kt & 1) * kAStage);
     mfma_step<MB>(fa1, fb1, acc);
     interleave_reads<MB, A_PER_WAVE>();
     sbi = sbn;

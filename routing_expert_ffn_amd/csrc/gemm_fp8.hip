@@ -77,6 +77,16 @@ __device__ __forceinline__ void copy_rows8(const uint8_t* base, const uint32_t (
   for (int i = I0; i < I0 + N; ++i) copy16(reinterpret_cast<const bf16*>(base + off[i]), dst + i * 1024);
 }
 
+// The same through a buffer resource: copy i reads byte voff[i] + soff
+// (zeros for a row past the tile's end, whose offset is out of range).
+template <int I0, int N, int M>
+__device__ __forceinline__ void copy_rows8_buf(__amdgpu_buffer_rsrc_t r, const uint32_t (&voff)[M], uint32_t soff,
+                                               char* dst) {
+  static_assert(I0 + N <= M, "copy range");
+#pragma unroll
+  for (int i = I0; i < I0 + N; ++i) copy16_buf(r, voff[i], soff, dst + i * 1024);
+}
+
 // Fragments of one 64-wide sub-step: lane half hf of row r takes the 16-byte
 // chunks 4s + hf and 4s + 2 + hf of the row (the MFMA's K order: bytes 0-15
 // of the operand are K 32j + 16hf + i of the block's first 32, bytes 16-31
@@ -180,22 +190,23 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   const int lrow = lane >> 3;
   const int wr = wave & 1, wc = wave >> 1;
 
-  const uint8_t* abase;
+  // A rows through a buffer resource: the rows of the tile past `rows` read
+  // as zero codes (no memory traffic, zeros into the matrix cores)
+  __amdgpu_buffer_rsrc_t arsrc;
   uint32_t aoff[A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < A_PER_WAVE; ++i) {
     const int r = (wave * A_PER_WAVE + i) * 8 + lrow;
-    const int rr = min(r, rows - 1);
-    const int chunk = (lane & 7) ^ swz_of_row(r);
+    const uint32_t chunk = (uint32_t)((lane & 7) ^ swz_of_row(r)) * 16u;
     if constexpr (GATEUP)
-      aoff[i] = (uint32_t)a.row_token[row0 + rr] * (uint32_t)K + chunk * 16;
+      aoff[i] = r < rows ? (uint32_t)a.row_token[row0 + r] * (uint32_t)K + chunk : kOutOfRange;
     else
-      aoff[i] = (uint32_t)rr * (uint32_t)K + chunk * 16;
+      aoff[i] = r < rows ? (uint32_t)r * (uint32_t)K + chunk : kOutOfRange;
   }
   if constexpr (GATEUP)
-    abase = static_cast<const uint8_t*>(a.a);
+    arsrc = raw_rsrc(a.a, a.a_bytes);
   else
-    abase = static_cast<const uint8_t*>(a.a) + (int64_t)row0 * K;
+    arsrc = raw_rsrc(static_cast<const uint8_t*>(a.a) + (int64_t)row0 * K, (uint32_t)rows * (uint32_t)K);
 
   const uint8_t* bbase;
   uint32_t boff[B_PER_WAVE];
@@ -253,10 +264,10 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   load_scale_group<MB, GATEUP>(a, sidx, bw0, bw1, 0, ga, gb0, gb1);
   // prologue: A and B of steps 0 and 1 in the order of the main loop (B of a
   // step before its A), then wait for step 0
-  copy_rows8<0, A_PER_WAVE>(abase, aoff, a_dst);
+  copy_rows8_buf<0, A_PER_WAVE>(arsrc, aoff, 0, a_dst);
   copy_rows8<0, B_PER_WAVE>(bbase, boff, b_dst);
   copy_rows8<0, B_PER_WAVE>(bbase + min(1, nk - 1) * kRowBytes, boff, b_dst + kBStage);
-  copy_rows8<0, A_PER_WAVE>(abase + min(1, nk - 1) * kRowBytes, aoff, a_dst + kAStage);
+  copy_rows8_buf<0, A_PER_WAVE>(arsrc, aoff, min(1, nk - 1) * kRowBytes, a_dst + kAStage);
   wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
   __builtin_amdgcn_s_barrier();
 
@@ -304,7 +315,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
     // barrier of the step after next.
     if (first) load_scale_group<MB, GATEUP>(a, sidx, bw0, bw1, min((kt >> 2) + 1, ng - 1), na, nb0, nb1);
     load_frags8<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, s00, s01, fa0, fb0);
-    copy_rows8<0, A_PER_WAVE>(abase + min(kt + 2, nk - 1) * kRowBytes, aoff, a_dst + (kt & 1) * kAStage);
+    copy_rows8_buf<0, A_PER_WAVE>(arsrc, aoff, min(kt + 2, nk - 1) * kRowBytes, a_dst + (kt & 1) * kAStage);
     mfma_step8<MB>(fa1, fb1, sa_k, sb_k, acc);
     if constexpr (j == 0)
       interleave8<MB, A_PER_WAVE, NSL>();

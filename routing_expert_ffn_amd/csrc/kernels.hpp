@@ -93,6 +93,7 @@ struct GemmArgs {
   int n_exp;                // E + S
   int n_tiles;              // column tiles per m-tile
   const void* a;            // gate/up: x [T,H]; down: h [rows,I]
+  uint32_t a_bytes;         // gate/up: bytes of x (< 2^31: the gather addresses it through one buffer resource)
   const int32_t* row_token; // gate/up: token of every row
   const void* b0;           // gate/up: w_gate; down: w_down
   const void* b1;           // gate/up: w_up; down: unused
