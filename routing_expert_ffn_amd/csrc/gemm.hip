@@ -113,9 +113,10 @@ __device__ __forceinline__ void interleave_reads() {
 // flight, so every copy has at least a full step to land.
 
 // One output tile: rows [row0, row0 + rows) of expert e, column tile nt.  WM
-// is the row count per wavefront: kWM for a full tile (2*kWM rows), kWM/2 for
-// a tile of at most kWM rows (an expert's last, short row tile), which then
-// costs half the MFMAs instead of computing padding.
+// is the row count per wavefront: kWM for a full tile (2*kWM rows); for an
+// expert's last row tile 3*kWM/4 when it has at most 3*kWM/2 rows and kWM/2
+// when it has at most kWM, which then costs three quarters or half of the
+// MFMAs instead of computing padding.
 template <int WM, bool GATEUP>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, int nt, int row0, int rows) {
   constexpr int BM = 2 * WM;
@@ -287,7 +288,12 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
   Work w;
   if (!work_of_block(a, 2 * kWM, w)) return;
   if (!w.pair) {
-    gemm_tile<kWM, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+    // an expert's last row tile of 129-192 rows runs three 32-row blocks per
+    // wavefront instead of four (a quarter less MFMA work on padding rows)
+    if (w.rows > 3 * kWM / 2)
+      gemm_tile<kWM, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+    else
+      gemm_tile<3 * kWM / 4, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
   } else {
     gemm_tile<kWM / 2, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
     if (w.nt + 1 < a.n_tiles) {

@@ -413,7 +413,11 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_fp8(GemmArgs a) {
   Work w;
   if (!work_of_block(a, 2 * kWM, w)) return;
   if (!w.pair) {
-    gemm_tile_fp8<kWM, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+    // a last row tile of 129-192 rows: three 32-row blocks per wavefront
+    if (w.rows > 3 * kWM / 2)
+      gemm_tile_fp8<kWM, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+    else
+      gemm_tile_fp8<3 * kWM / 4, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
   } else {
     gemm_tile_fp8<kWM / 2, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
     if (w.nt + 1 < a.n_tiles) {

@@ -87,21 +87,38 @@ def _oracle_rows(shape, inp, e, toks):
                                      lambda ee: tuple(to_oracle(inp[n][ee]) for n in names))
 
 
+def _exact_inputs(shape, inp, seed, large_gate=False):
+    """Codes and scales for which every product and partial sum is exact in
+    the matrix cores (weights in {0, +-0.5, +-1} times 2^-6 .. 2^-4, x in
+    {0, +-1, +-2} with a 7 in every 128-wide tile, which quantises exactly).
+    large_gate: x in {1, 2} and W_gate in {0.5, 1} x 2^-1, so every gate value
+    is at least 64 and silu(g) = g exactly in fp32 and fp64: h = g*u is then
+    the same fp32 value on both sides and no h code can round differently."""
+    T, E, S, H, I = shape.T, shape.E, shape.S, shape.H, shape.I
+    rng = np.random.default_rng(seed)
+    for n, shp in (("w_gate", (E + S, I, H)), ("w_up", (E + S, I, H)), ("w_down", (E + S, H, I))):
+        sn = "s" + n[1:]
+        if large_gate and n == "w_gate":
+            inp[n] = _codes(rng.choice([0.5, 1.0], shp)).cuda()
+            inp[sn] = torch.full(tuple(inp[sn].shape), 126, dtype=torch.uint8).cuda()
+            continue
+        inp[n] = _codes(rng.choice([-1.0, -0.5, 0.0, 0.5, 1.0], shp)).cuda()
+        inp[sn] = torch.from_numpy(rng.integers(121, 124, tuple(inp[sn].shape)).astype(np.uint8)).cuda()
+    vals = [1.0, 2.0] if large_gate else [-2.0, -1.0, 0.0, 1.0, 2.0]
+    xv = rng.choice(vals, (T, H)).astype(np.float32)
+    xv[:, ::128] = 7.0                           # tile maximum 7 = 448 * 2^-6: x quantises exactly
+    inp["x"] = torch.from_numpy(xv).to(torch.bfloat16).cuda()
+
+
 def test_expert_stage_exact_arithmetic():
     """Codes and scales chosen so that every product and partial sum is exact
     in the matrix cores: the expert rows then match the oracle to rounding,
     on full and half-height row tiles and the shared expert."""
     shape = TEST_SHAPES["v3_fp8_small"].with_(T=600)
     inp = make_inputs(shape, device="cuda")
-    T, E, S, H, I = shape.T, shape.E, shape.S, shape.H, shape.I
-    rng = np.random.default_rng(9)
-    for n, shp in (("w_gate", (E + S, I, H)), ("w_up", (E + S, I, H)), ("w_down", (E + S, H, I))):
-        inp[n] = _codes(rng.choice([-1.0, -0.5, 0.0, 0.5, 1.0], shp)).cuda()
-        sn = "s" + n[1:]
-        inp[sn] = torch.from_numpy(rng.integers(121, 124, tuple(inp[sn].shape)).astype(np.uint8)).cuda()
-    xv = rng.choice([-2.0, -1.0, 0.0, 1.0, 2.0], (T, H)).astype(np.float32)
-    xv[:, ::128] = 7.0                           # tile maximum 7 = 448 * 2^-6: x quantises exactly
-    inp["x"] = torch.from_numpy(xv).to(torch.bfloat16).cuda()
+    E = shape.E
+    T = shape.T
+    _exact_inputs(shape, inp, 9)
     idx = _routing(shape, 3)
     y, off, rt = _stage(shape, inp, idx)
     for e in (7, int(idx[100, 1]), E):
@@ -176,3 +193,33 @@ def test_expert_stage_random_codes():
         err = np.abs(y[rows] - ref) / rms
         print("expert %d: %d rows, max err %.3g, mean %.3g x RMS" % (e, len(rows), err.max(), err.mean()))
         assert err.max() <= 6e-2 and err.mean() <= 2e-3
+
+
+def test_expert_stage_row_tile_boundaries():
+    """FP8 experts whose row counts sit on and around the row-tile sizes:
+    full 256-row tiles, last tiles of 129-192 rows (three 32-row blocks per
+    wavefront) and short last tiles of at most 128 rows (half height, pairs
+    of column tiles).  Exact-arithmetic inputs with large gate values, so h
+    is the same on both sides and every row matches the oracle to rounding
+    (random codes at I = 256 let single h codes round to neighbouring E4M3
+    values on the two sides, which moves an output by up to ~0.1 x RMS)."""
+    counts = [128, 256, 129, 1, 0, 127, 255, 257, 384, 160, 192, 193, 448, 449, 577]
+    E = len(counts)
+    T = max(counts)
+    shape = TEST_SHAPES["v3_fp8_small"].with_(T=T, E=E, S=1, k=E, G=1, topk_group=1, H=256, I=256)
+    idx = np.full((T, E), -1, np.int32)
+    for t in range(T):
+        es = [e for e in range(E) if t < counts[e]]
+        idx[t, :len(es)] = es
+    inp = make_inputs(shape, device="cuda")
+    _exact_inputs(shape, inp, 21, large_gate=True)
+    y, off, rt = _stage(shape, inp, idx)
+    assert np.diff(off[:E + 1]).tolist() == counts
+    for e in list(range(E)) + [E]:
+        rows = _expert_rows(shape, e, off, T)
+        if rows.size == 0:
+            continue
+        ref = _oracle_rows(shape, inp, e, rt[rows].astype(np.int64))
+        rms = np.sqrt(np.mean(ref ** 2))
+        err = np.abs(y[rows] - ref) / rms
+        assert err.max() <= 1e-3, (e, counts[e] if e < E else T, err.max())

@@ -464,10 +464,11 @@ def test_native_library_is_the_one_loaded():
 
 def test_expert_ffn_row_tile_boundaries():
     """Experts whose row counts sit on and around the row-tile sizes (full
-    256-row tiles, and the short last tiles of at most 128 rows that run at
-    half height in pairs of column tiles)."""
+    256-row tiles, last tiles of 129-192 rows that run three 32-row blocks per
+    wavefront, and the short last tiles of at most 128 rows that run at half
+    height in pairs of column tiles)."""
     from workloads import LayerShape
-    counts = [128, 256, 129, 1, 0, 127, 255, 257, 384, 385, 513, 540, 577, 1050]
+    counts = [128, 256, 129, 1, 0, 127, 255, 257, 384, 385, 513, 540, 577, 1050, 160, 192, 193, 448, 449]
     E = len(counts)
     T = max(counts)
     shape = LayerShape("tb", T=T, H=256, E=E, S=1, k=E, I=256)
