@@ -13,12 +13,13 @@
 //            the two projections;
 //   down     h rows are contiguous per expert; y_rows = h W_down^T (fp32).
 // bf16 tiles: 4 wavefronts, block tile BM x 256 (B rows) x 64 (K), each wave
-// WM x 128 on v_mfma_f32_32x32x16_bf16, operands double-buffered in LDS with
-// an XOR swizzle (conflict-free 16-byte reads), global loads for step k+1 in
-// flight while step k computes.  Work items (see work_of_block) are ordered
-// so that each XCD (one L2) walks a contiguous range in which the row tiles
-// sharing a weight tile, and the column tiles sharing an input row tile, run
-// side by side and re-read the shared operand from L2.
+// WM x 128 on v_mfma_f32_32x32x16_bf16, operands staged in LDS (two A and
+// three B stages) with an XOR swizzle (conflict-free 16-byte reads), the
+// copies for step k+2 in flight while step k computes.  Work items (see
+// work_of_block) are ordered so that each XCD (one L2) walks a contiguous
+// range in which the row tiles sharing a weight tile, and the column tiles
+// sharing an input row tile, run side by side and re-read the shared operand
+// from L2.
 #include "common.hpp"
 #include "gemm_sched.hpp"
 #include "kernels.hpp"
@@ -30,10 +31,9 @@ constexpr int kRowBytes = kBK * 2;     // bytes of one tile row in LDS
 constexpr int kBNB = 256;              // B rows per block tile
 constexpr int kWM = 128;               // rows per wavefront (bf16 path); BM = 2 * kWM
 // LDS: two A stages (input rows) and three B stages (weight rows), 32 KB
-// each, 160 KB in all.  A row tile is shared by all column tiles of an
-// expert and mostly hits L2; a weight tile is shared by the expert's few row
-// tiles and more often comes from HBM, so weights are copied two steps ahead
-// of use and inputs one step ahead.
+// each, 160 KB in all.  Both operands are copied two steps ahead of use: B
+// into the stage freed one step earlier (three stages), A right after the
+// barrier that frees its stage (two stages).
 constexpr int kAStage = 2 * kWM * kRowBytes;
 constexpr int kBStage = kBNB * kRowBytes;
 constexpr int kAStages = 2, kBStages = 3;
