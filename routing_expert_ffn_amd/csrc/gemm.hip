@@ -39,6 +39,10 @@ constexpr int kBStage = kBNB * kRowBytes;
 constexpr int kAStages = 2, kBStages = 3;
 constexpr int kLdsBytes = kAStages * kAStage + kBStages * kBStage;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
+// epilogue staging: one region per wavefront for its bf16 sub-tile of up to
+// kWM rows x 128 columns, rows padded by 16 bytes
+constexpr int kEpWave = kWM * (128 * 2 + 16);
+static_assert(4 * kEpWave <= kLdsBytes, "epilogue staging fits in the stages");
 
 // Copies I0 .. I0+N-1 of a wave's group: copy i reads base + off[i] and
 // fills the 1 KB of LDS at dst + i*1024.
@@ -252,32 +256,68 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   // no copy may still be writing LDS when the stages are reused or released
   wait_vmem_upto<0>();
 
+  // Epilogue through LDS for the bf16 outputs (h, routed expert rows): once
+  // every wave is done with the stages, each wave stages its sub-tile in an
+  // LDS region of its own (rows padded by 16 bytes against bank conflicts)
+  // and writes it back as whole row segments with 16-byte stores -- an
+  // eighth of the store instructions of writing the MFMA layout (one value
+  // per lane, rows apart) directly, which kept the address unit busy for
+  // several microseconds per tile.  fp32 rows (shared experts) are written
+  // directly: staging them in two passes cost more registers than it saved.
+  __syncthreads();
+  char* const ep = lds + wave * kEpWave;
+  const int rl = 4 * (lane >> 5), cl = lane & 31;  // the lane's row offset and column in a 32 x 32 block
+  const int rows_w = rows - wr * WM;               // rows of this wave's sub-tile that exist (may be <= 0)
+  if constexpr (GATEUP) {
+    // h = silu(g) * u: WM rows x 64 columns (h columns wc*64 .. +63 of the tile's 128)
+    constexpr int P = 64 * 2 + 16;
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wr * WM + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= rows) continue;
-      if constexpr (GATEUP) {
-        bf16* orow = static_cast<bf16*>(a.c) + (int64_t)(row0 + row) * a.N;
+      for (int r = 0; r < 16; ++r)
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const float g = acc[m][n][r], u = acc[m][n + 2][r];
-          const float hv = g / (1.0f + __expf(-g)) * u;
-          orow[nt * 128 + wc * 64 + n * 32 + (lane & 31)] = (bf16)hv;
+          *reinterpret_cast<bf16*>(ep + (m * 32 + 8 * (r >> 2) + rl + (r & 3)) * P + (n * 32 + cl) * 2) =
+              (bf16)(g / (1.0f + __expf(-g)) * u);
         }
-      } else if (a.c16 == nullptr || e >= a.n_routed) {
-        // fp32 expert rows (shared experts' rows at row - routed_rows when
-        // the routed rows go to c16)
-        const int64_t orow_i = (int64_t)(row0 + row) - (a.c16 ? a.routed_rows : 0);
-        float* orow = static_cast<float*>(a.c) + orow_i * a.N;
+    bf16* const cw = static_cast<bf16*>(a.c) + (int64_t)(row0 + wr * WM) * a.N + nt * 128 + wc * 64;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = acc[m][n][r];
-      } else {
-        bf16* orow = static_cast<bf16*>(a.c16) + (int64_t)(row0 + row) * a.N;
+    for (int i = 0; i < WM * 8 / 64; ++i) {
+      const int idx = i * 64 + lane, row = idx >> 3, ch = idx & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ep + row * P + ch * 16);
+      if (row < rows_w) *reinterpret_cast<u32x4*>(cw + (int64_t)row * a.N + ch * 8) = v;
+    }
+  } else if (a.c16 == nullptr || e >= a.n_routed) {
+    // fp32 expert rows written directly from the MFMA layout
+    float* const cw = static_cast<float*>(a.c) + ((int64_t)(row0 + wr * WM) - (a.c16 ? a.routed_rows : 0)) * a.N +
+                      nt * kBNB + wc * 128 + cl;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = (bf16)acc[m][n][r];
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m * 32 + 8 * (r >> 2) + rl + (r & 3);
+        if (row >= rows_w) continue;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) cw[(int64_t)row * a.N + n * 32] = acc[m][n][r];
       }
+  } else {
+    // bf16 routed rows: WM rows x 128 columns
+    constexpr int P = 128 * 2 + 16;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          *reinterpret_cast<bf16*>(ep + (m * 32 + 8 * (r >> 2) + rl + (r & 3)) * P + (n * 32 + cl) * 2) =
+              (bf16)acc[m][n][r];
+    bf16* const cw = static_cast<bf16*>(a.c16) + (int64_t)(row0 + wr * WM) * a.N + nt * kBNB + wc * 128;
+#pragma unroll
+    for (int i = 0; i < WM * 16 / 64; ++i) {
+      const int idx = i * 64 + lane, row = idx >> 4, ch = idx & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ep + row * P + ch * 16);
+      if (row < rows_w) *reinterpret_cast<u32x4*>(cw + (int64_t)row * a.N + ch * 8) = v;
     }
   }
 }
