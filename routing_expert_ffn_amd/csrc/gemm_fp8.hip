@@ -50,6 +50,7 @@ constexpr int kBStage = kBNB * kRowBytes;
 constexpr int kAStages = 2, kBStages = 3;
 constexpr int kLdsBytes = kAStages * kAStage + kBStages * kBStage;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(4 * kWM * (128 * 2 + 16) <= kLdsBytes, "down epilogue staging fits in the stages");
 
 // Exponent p of the UE8M0 scale of a tile whose largest magnitude is amax:
 // the smallest p >= -127 with amax / 2^p <= 448 (= 1.75 * 2^8); a zero or
@@ -385,24 +386,44 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
       }
       a.sc[((int64_t)(nt >> 2) * a.n_rows + row0 + row) * 4 + (nt & 3)] = (uint8_t)(p + 127);
     }
-  } else {
+  } else if (a.c16 == nullptr || e >= a.n_routed) {
+    // fp32 expert rows (shared experts' rows at row - routed_rows when the
+    // routed rows go to c16), written directly from the MFMA layout
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wr * WM + m * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
         if (row >= rows) continue;
-        if (a.c16 == nullptr || e >= a.n_routed) {
-          const int64_t orow_i = (int64_t)(row0 + row) - (a.c16 ? a.routed_rows : 0);
-          float* orow = static_cast<float*>(a.c) + orow_i * a.N;
+        const int64_t orow_i = (int64_t)(row0 + row) - (a.c16 ? a.routed_rows : 0);
+        float* orow = static_cast<float*>(a.c) + orow_i * a.N;
 #pragma unroll
-          for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = acc[m][n][r];
-        } else {
-          bf16* orow = static_cast<bf16*>(a.c16) + (int64_t)(row0 + row) * a.N;
-#pragma unroll
-          for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = (bf16)acc[m][n][r];
-        }
+        for (int n = 0; n < 4; ++n) orow[nt * kBNB + wc * 128 + n * 32 + (lane & 31)] = acc[m][n][r];
       }
+    }
+  } else {
+    // bf16 routed rows through LDS: each wave stages its WM x 128 sub-tile in
+    // a region of its own (rows padded by 16 bytes) and writes whole row
+    // segments with 16-byte stores (an eighth of the store instructions of
+    // writing the MFMA layout directly)
+    constexpr int P = 128 * 2 + 16;
+    __syncthreads();  // every wave is done with the stages
+    char* const ep = lds + wave * (kWM * P);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          *reinterpret_cast<bf16*>(ep + (m * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)) * P + (n * 32 + (lane & 31)) * 2) =
+              (bf16)acc[m][n][r];
+    const int rows_w = rows - wr * WM;  // rows of this wave's sub-tile that exist (may be <= 0)
+    bf16* const cw = static_cast<bf16*>(a.c16) + (int64_t)(row0 + wr * WM) * a.N + nt * kBNB + wc * 128;
+#pragma unroll
+    for (int i = 0; i < WM * 16 / 64; ++i) {
+      const int idx = i * 64 + lane, row = idx >> 4, ch = idx & 15;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(ep + row * P + ch * 16);
+      if (row < rows_w) *reinterpret_cast<i32x4*>(cw + (int64_t)row * a.N + ch * 8) = v;
     }
   }
 }
