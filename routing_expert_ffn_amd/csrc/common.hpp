@@ -82,6 +82,15 @@ __device__ __forceinline__ uint64_t rank_key(float score, int e) {
 }
 __device__ __forceinline__ int key_expert(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu)); }
 
+// SwiGLU of one gate/up pair: silu(g) * u = g * u / (1 + e^-g), the
+// reciprocal from v_rcp_f32 (about 1 ulp) instead of a correctly rounded
+// division: the result is rounded to bf16 or E4M3 next, and the division's
+// refinement steps cost ~15 VALU instructions for each of the 128 values a
+// lane produces per tile.  Large negative g gives e^-g = inf, rcp = 0: -0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // ---- global->LDS staging of 128-byte tile rows (grouped GEMMs, router GEMM)
 
 typedef __attribute__((address_space(3))) void lds_void_t;

@@ -279,7 +279,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
         for (int n = 0; n < 2; ++n) {
           const float g = acc[m][n][r], u = acc[m][n + 2][r];
           *reinterpret_cast<bf16*>(ep + (m * 32 + 8 * (r >> 2) + rl + (r & 3)) * P + (n * 32 + cl) * 2) =
-              (bf16)(g / (1.0f + __expf(-g)) * u);
+              (bf16)swiglu(g, u);
         }
     bf16* const cw = static_cast<bf16*>(a.c) + (int64_t)(row0 + wr * WM) * a.N + nt * 128 + wc * 64;
 #pragma unroll

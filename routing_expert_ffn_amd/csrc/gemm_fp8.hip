@@ -357,7 +357,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const float g = acc[m][n][r], u = acc[m][n + 2][r];
-          tile[row * kTS + wc * 64 + n * 32 + (lane & 31)] = g / (1.0f + __expf(-g)) * u;
+          tile[row * kTS + wc * 64 + n * 32 + (lane & 31)] = swiglu(g, u);
         }
       }
     __syncthreads();
