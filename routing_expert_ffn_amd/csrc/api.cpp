@@ -126,7 +126,7 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
 
 struct Layout {
   size_t logits, rpart, cand, idx, w, counts, offsets, slot_row, row_token, chunk_cnt, chunk_base, seg_start, seg_len,
-      f_prefix, h_prefix, h, y, xq, sx, sxr, sh, sbg, sbu, sbd, dcnt, total;
+      f_prefix, h_prefix, pool, h, y, xq, sx, sxr, sh, sbg, sbu, sbd, dcnt, total;
 };
 
 // bytes of a grouped row-space scale array (4-step groups of K/128 blocks)
@@ -170,6 +170,7 @@ Layout layout_of(const Dims& d) {
   L.seg_len = take((E + S) * 4);
   L.f_prefix = take((E + S + 1) * 4);
   L.h_prefix = take((E + S + 1) * 4);
+  L.pool = take(2 * 4);  // item counters of the two GEMMs' shared pools
   L.dcnt = take(E * 4);  // drop mode: assignments per expert before the limit
   L.h = take(rows * (size_t)d.I * (d.fp8 ? 1 : d.esz));  // FP8: E4M3 codes of h
   L.y = take(rows * (size_t)d.H * 4);  // expert outputs are fp32
@@ -468,6 +469,7 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   sa.seg_len = at<int32_t>(ws, L.seg_len);
   sa.f_prefix = at<int32_t>(ws, L.f_prefix);
   sa.h_prefix = at<int32_t>(ws, L.h_prefix);
+  sa.pool = at<int32_t>(ws, L.pool);
   e = timed(K_SCHEDULE, s, [&] { return launch_schedule(sa, s); });
   if (e != hipSuccess) return hip_fail(e, "schedule launch");
   const int64_t bound = gemm_mtile_bound((int)d.T, d.E, d.S, d.k, BM);
@@ -478,6 +480,9 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   g.f_prefix = sa.f_prefix;
   g.h_prefix = sa.h_prefix;
   g.row_token = row_token;
+  // bf16 and FP8 kernels share each GEMM's last items between the XCDs
+  // (the fp32 kernel has no LDS to broadcast the counter)
+  g.pool = d.dtype != MOE_F32 ? sa.pool : nullptr;
   void* h = at<void>(ws, L.h);
   // gate/up + SwiGLU
   g.K = d.H;
@@ -500,6 +505,7 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   e = timed(K_GATEUP, s, [&] { return launch_gateup(g, d.dtype, bound, s); });
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
   // down
+  if (g.pool) g.pool = sa.pool + 1;
   g.K = d.I;
   g.N = d.H;
   g.n_tiles = d.dtype != MOE_F32 ? d.H / 256 : d.H / 32;

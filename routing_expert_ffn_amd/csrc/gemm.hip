@@ -326,7 +326,7 @@ template <bool GATEUP>
 __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   Work w;
-  if (!work_of_block(a, 2 * kWM, w)) return;
+  if (!work_of_block(a, 2 * kWM, w, reinterpret_cast<int*>(lds))) return;
   if (!w.pair) {
     // an expert's last row tile of 129-192 rows runs three 32-row blocks per
     // wavefront instead of four (a quarter less MFMA work on padding rows)
@@ -381,10 +381,11 @@ __global__ __launch_bounds__(64) void expert_gemm_f32(GemmArgs a) {
 }
 
 // Segments of every expert and the exclusive prefixes of its full and short
-// row-tile counts.
+// row-tile counts; clears the pool counters of the two GEMMs that follow.
 __global__ __launch_bounds__(1024) void schedule_kernel(ScheduleArgs a) {
   __shared__ int32_t bf[2][1024], bh[2][1024];
   const int tid = threadIdx.x;
+  if (tid < 2) a.pool[tid] = 0;  // the two GEMMs' pool counters
   const int n_exp = a.E + a.S;
   int carry_f = 0, carry_h = 0;
   for (int e0 = 0; e0 < n_exp; e0 += 1024) {

@@ -432,7 +432,7 @@ template <bool GATEUP>
 __global__ __launch_bounds__(256, 1) void expert_gemm_fp8(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   Work w;
-  if (!work_of_block(a, 2 * kWM, w)) return;
+  if (!work_of_block(a, 2 * kWM, w, reinterpret_cast<int*>(lds))) return;
   if (!w.pair) {
     // a last row tile of 129-192 rows: three 32-row blocks per wavefront
     if (w.rows > 3 * kWM / 2)

@@ -27,14 +27,60 @@ __device__ __forceinline__ int items_before(const GemmArgs& a, int e, int np) {
   return a.f_prefix[e] * a.n_tiles + a.h_prefix[e] * np;
 }
 
-__device__ __forceinline__ bool work_of_block(const GemmArgs& a, int BM, Work& w) {
+// Item of the workgroup.  XCD x (blocks x, x+8, ...: the hardware hands
+// blocks to the eight XCDs in turn) owns the contiguous range of n_x items
+// starting at start_x, and its blocks take them in order.  With a pool, the
+// last ceil(n_x/16) items of every range are shared instead: blocks past
+// their XCD's own part take pool items through one atomic counter, so an XCD
+// that runs ahead finishes the others' last items (the XCDs progress at
+// different rates, and the kernel ends with the slowest).  `slot` is one int
+// of LDS that broadcasts the counter value to the workgroup (the stages are
+// not in use yet).  Every item is taken exactly once: the counter hands out
+// each pool index once, and every XCD has at least its own share of takers
+// (its last blocks) because the grid is at least the item count.
+__device__ __forceinline__ bool work_of_block(const GemmArgs& a, int BM, Work& w, int* slot = nullptr) {
   const int ntn = a.n_tiles;
   const int np = (ntn + 1) >> 1;
   const int total = items_before(a, a.n_exp, np);
   const int bid = blockIdx.x;
-  if (bid >= total) return false;
-  const int xcd = bid & 7, q = total >> 3, r = total & 7;
-  const int L = xcd * q + min(xcd, r) + (bid >> 3);
+  const int xcd = bid & 7, q = total >> 3, r = total & 7, local = bid >> 3;
+  const int nx = q + (xcd < r ? 1 : 0);
+  int L;
+  if (a.pool == nullptr) {
+    if (local >= nx) return false;  // the same as bid >= total
+    L = xcd * q + min(xcd, r) + local;
+  } else {
+    const int tx = (nx + 15) >> 4;
+    if (local < nx - tx) {
+      L = xcd * q + min(xcd, r) + local;
+    } else {
+      // at most twice its own share of takers per XCD (its own last blocks
+      // and as many surplus blocks): enough for an XCD that runs ahead to take
+      // a second share, while the surplus blocks beyond them leave without
+      // touching the contended counter
+      if (local >= nx + tx) return false;
+      // pool size: the shares of the eight ranges (q or q + 1 items each)
+      const int tq = (q + 15) >> 4, tq1 = (q + 16) >> 4;
+      const int pool_total = r * tq1 + (8 - r) * tq;
+      if (threadIdx.x == 0) *slot = atomicAdd(a.pool, 1);
+      __syncthreads();
+      const int i = __builtin_amdgcn_readfirstlane(*slot);
+      __syncthreads();  // every thread has the value before the stages are written
+      if (i >= pool_total) return false;
+      // pool index i: the shares of XCDs 0..7 in order
+      L = -1;
+      int base = 0;
+      for (int x = 0; x < 8; ++x) {
+        const int n = q + (x < r ? 1 : 0), t = (n + 15) >> 4;
+        if (i < base + t) {
+          L = x * q + min(x, r) + (n - t) + (i - base);
+          break;
+        }
+        base += t;
+      }
+      if (L < 0) return false;
+    }
+  }
   // largest e with items_before(e) <= L (experts without items are skipped)
   int lo = 0, hi = a.n_exp;
   while (hi - lo > 1) {
@@ -71,6 +117,13 @@ __device__ __forceinline__ bool work_of_block(const GemmArgs& a, int BM, Work& w
     w.rows = len - F * BM;
     w.pair = true;
   }
+  // the same in every lane: keep the item (and the addresses and buffer
+  // resources derived from it) in scalar registers; a resource the compiler
+  // takes for divergent costs a waterfall loop around every copy
+  w.e = __builtin_amdgcn_readfirstlane(w.e);
+  w.nt = __builtin_amdgcn_readfirstlane(w.nt);
+  w.row0 = __builtin_amdgcn_readfirstlane(w.row0);
+  w.rows = __builtin_amdgcn_readfirstlane(w.rows);
   return true;
 }
 

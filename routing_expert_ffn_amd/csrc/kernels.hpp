@@ -86,6 +86,7 @@ struct ScheduleArgs {
   int32_t* seg_len;         // [E+S]
   int32_t* f_prefix;        // [E+S+1] full row tiles before expert e
   int32_t* h_prefix;        // [E+S+1] short row tiles before expert e
+  int32_t* pool;            // [2] item counters of the two GEMMs' shared pools, zeroed here
 };
 
 struct GemmArgs {
@@ -117,6 +118,10 @@ struct GemmArgs {
   const uint8_t* sb0;       // [n_exp, N/128, roundup(K/128, 4)] scales of b0, 4-byte aligned
   const uint8_t* sb1;       // the same for b1 (gate/up)
   uint8_t* sc;              // gate/up: grouped [ceil(N/512), n_rows, 4] scales of h
+  // counter of the shared pool of items (the last sixteenth of every XCD's
+  // range, taken by whichever XCD gets there first), zeroed before the
+  // launch; null: every item stays with its XCD
+  int32_t* pool;
 };
 
 // Weight scales repacked with rows padded to 4 bytes (three matrices).
