@@ -223,6 +223,44 @@ def test_expert_ffn_stage_rows():
         assert err <= 2e-2 * rms + np.max(bf16_half_ulp(ref)), (e, err / rms)
 
 
+def test_expert_ffn_gathers_x_up_to_2gib():
+    """The gate/up GEMM gathers token rows through one 32-bit buffer resource
+    over x: with x just under 2 GiB (149796 tokens of H = 7168), the rows of
+    the last tokens, whose byte offsets approach 2^31, and a random sample of
+    others match the oracle.  (One token more is rejected before any launch:
+    test_abi.)"""
+    from workloads import LayerShape
+    H, I = 7168, 128
+    T = (2 ** 31 - 1) // (H * 2)
+    assert T * H * 2 < 2 ** 31 and (T + 1) * H * 2 >= 2 ** 31
+    shape = LayerShape("x_2gib", T=T, H=H, E=2, S=0, k=1, I=I)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    x = (torch.randn(T, H, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    wg = (torch.randn(2, I, H, device="cuda", generator=g) / H ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn(2, I, H, device="cuda", generator=g) / H ** 0.5).to(torch.bfloat16)
+    wd = (torch.randn(2, H, I, device="cuda", generator=g) / I ** 0.5).to(torch.bfloat16)
+    idx = (torch.arange(T, device="cuda", dtype=torch.int32) % 2).view(T, 1)
+    cfg = moe.make_config(shape)
+    counts, offsets, row_token, slot_row = moe.permute(cfg, idx)
+    y = moe.expert_ffn(cfg, x, wg, wu, wd, offsets, row_token)
+    torch.cuda.synchronize()
+    off, rt = offsets.cpu().numpy(), row_token.cpu().numpy()
+    rng = np.random.default_rng(5)
+    for e in (0, 1):
+        seg = np.arange(off[e], off[e + 1])
+        rows = np.concatenate([seg[-48:], rng.choice(seg[:-48], 16, replace=False)])
+        toks = rt[rows]
+        assert toks.max() >= T - 2
+        yr = y[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+        ref = oracle.expert_rows(shape, to_oracle(x[torch.from_numpy(toks.astype(np.int64)).cuda()]),
+                                 to_oracle(wg[e]), to_oracle(wu[e]), to_oracle(wd[e]))
+        rms = np.sqrt(np.mean(ref ** 2))
+        err = np.max(np.abs(yr - ref))
+        assert err <= 2e-2 * rms, (e, err / rms)
+    del x, y
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_combine_stage(dtype):
     from workloads import LayerShape
