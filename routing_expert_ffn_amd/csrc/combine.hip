@@ -13,10 +13,17 @@
 
 namespace {
 
+constexpr int kSlotBatch = 8;  // routed rows loaded together per thread
+
 template <typename T>
 struct Vec8;
 template <>
 struct Vec8<bf16> {
+  struct Raw {
+    bf16x8 x;
+  };
+  static __device__ __forceinline__ Raw load_raw(const bf16* p) { return Raw{*reinterpret_cast<const bf16x8*>(p)}; }
+  static __device__ __forceinline__ float at(const Raw& r, int i) { return (float)r.x[i]; }
   static __device__ __forceinline__ void load(const bf16* p, float (&v)[8]) {
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
@@ -31,6 +38,13 @@ struct Vec8<bf16> {
 };
 template <>
 struct Vec8<float> {
+  struct Raw {
+    f32x4 a, b;
+  };
+  static __device__ __forceinline__ Raw load_raw(const float* p) {
+    return Raw{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+  }
+  static __device__ __forceinline__ float at(const Raw& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
   static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(p);
     const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
@@ -66,18 +80,39 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
   TO* out = static_cast<TO*>(a.out) + (int64_t)t * a.H;
   for (int c = threadIdx.x * 8; c < a.H; c += blockDim.x * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    // every slot loads (an empty slot reads row 0 and discards it), so the
-    // loads of all slots can be in flight together
-    for (int j = 0; j < a.k; ++j) {
-      const int r = srow[j];
-      const bool live = r >= 0;
-      const float w = sw[j];
-      float v[8];
-      Vec8<TR>::load(y + (int64_t)(live ? r : 0) * a.H + c, v);
+    // the first shared expert's row is loaded with the first batch and
+    // added after the slots
+    typename Vec8<float>::Raw sh;
+    if (a.S > 0) sh = Vec8<float>::load_raw(a.y_shared + (int64_t)t * a.H + c);
+    // slots in batches of kSlotBatch: every slot of a batch loads (raw, no
+    // conversion, so no load waits for another) before any is added; an
+    // empty slot reads row 0 and discards it
+    for (int j0 = 0; j0 < a.k; j0 += kSlotBatch) {
+      typename Vec8<TR>::Raw v[kSlotBatch];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = live ? acc[i] + w * v[i] : acc[i];
+      for (int jj = 0; jj < kSlotBatch; ++jj) {
+        const int j = j0 + jj;
+        if (j < a.k) {
+          const int r = srow[j];
+          v[jj] = Vec8<TR>::load_raw(y + (int64_t)(r >= 0 ? r : 0) * a.H + c);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj) {
+        const int j = j0 + jj;
+        if (j < a.k) {
+          const bool live = srow[j] >= 0;
+          const float w = sw[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = live ? acc[i] + w * Vec8<TR>::at(v[jj], i) : acc[i];
+        }
+      }
     }
-    for (int s = 0; s < a.S; ++s) {
+    if (a.S > 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += Vec8<float>::at(sh, i);
+    }
+    for (int s = 1; s < a.S; ++s) {
       float v[8];
       Vec8<float>::load(a.y_shared + ((int64_t)s * a.T + t) * a.H + c, v);
 #pragma unroll

@@ -44,20 +44,56 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float v) {
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
-// Maximum of a 64-bit key over the wavefront (butterfly; every lane gets it).
+// Lane exchanges inside each row of 16 lanes through DPP, for reductions of
+// the whole (fully active) wavefront: lane ^ 1 and lane ^ 2 (quad
+// permutations [1,0,3,2] and [2,3,0,1]), then the mirror of each half row
+// (lane i <-> 7 - i) and of each row (i <-> 15 - i).  Once every lane of a
+// quad (of a half row) holds that quad's (half row's) reduction, the mirror
+// pairs it with the other quad (half row), so four exchanges reduce a row.
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum of a 64-bit key over the wavefront (every lane gets it): rows
+// reduced through DPP, then the four row maxima read out.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 1; off < MOE_WAVE; off <<= 1) {
-    uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = max_u64(v, dpp_u64<kDppQuadXor1>(v));
+  v = max_u64(v, dpp_u64<kDppQuadXor2>(v));
+  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+  v = max_u64(v, dpp_u64<kDppMirror>(v));
+  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int off = 1; off < MOE_WAVE; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {

@@ -100,6 +100,20 @@ __device__ __forceinline__ float ordered_to_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
+// The two largest of a multiset of ordered values, (m1 >= m2), merged with
+// another such pair.
+__device__ __forceinline__ void top2_merge(uint32_t& m1, uint32_t& m2, uint32_t o1, uint32_t o2) {
+  const uint32_t hi = m1 > o1 ? m1 : o1, lo = m1 > o1 ? o1 : m1;
+  const uint32_t r2 = m2 > o2 ? m2 : o2;
+  m2 = lo > r2 ? lo : r2;
+  m1 = hi;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void top2_step(uint32_t& m1, uint32_t& m2) {
+  top2_merge(m1, m2, dpp_u32<CTRL>(m1), dpp_u32<CTRL>(m2));
+}
+
 // Selection scores of one token: lane holds experts e = j*64 + lane.
 template <int NJ>
 __device__ __forceinline__ void token_scores(const RouteParams& p, const float* lrow, const float* sel_bias,
@@ -122,37 +136,78 @@ __device__ __forceinline__ void token_scores(const RouteParams& p, const float* 
     }
   }
   if (p.G <= 1) return;
-  // group scores: best and second best key of each group (an equal value at
-  // another index counts as the second best)
   const int gsz = p.gsz;
-  float my_gs = 0.0f;
-  for (int g = 0; g < p.G; ++g) {
-    uint64_t b1 = 0;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = j * MOE_WAVE + lane;
-      if (key[j] && e / gsz == g && key[j] > b1) b1 = key[j];
-    }
-    b1 = wave_max_u64(b1);
-    uint64_t b2 = 0;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = j * MOE_WAVE + lane;
-      if (key[j] && e / gsz == g && key[j] != b1 && key[j] > b2) b2 = key[j];
-    }
-    b2 = wave_max_u64(b2);
-    const float v1 = ordered_to_float((uint32_t)(b1 >> 32));
-    const float v2 = ordered_to_float((uint32_t)(b2 >> 32));
-    const float gs = v1 + v2;
-    if (lane == g) my_gs = gs;
-  }
-  uint64_t gkey = lane < p.G ? rank_key(my_gs, lane) : 0;
   uint64_t kept = 0;
-  for (int i = 0; i < p.topk_group; ++i) {
-    const uint64_t m = wave_max_u64(gkey);
-    const int g = key_expert(m);
-    kept |= 1ull << g;
-    if (lane == g) gkey = 0;
+  if ((gsz & (gsz - 1)) == 0 && gsz >= 2 && gsz <= MOE_WAVE && p.G * gsz == p.E) {
+    // power-of-two groups inside a register: the expert of (j, lane) is in
+    // group j*R + lane/gsz, R = 64/gsz.  Each group's two best values are
+    // merged in place across its gsz lanes (the top two of a multiset, so an
+    // equal value at another index is the second best); the group score is
+    // the fp32 sum of the two; lane g then takes group g's score.
+    const int R = MOE_WAVE / gsz;
+    float my_gs = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      uint32_t m1 = (uint32_t)(key[j] >> 32), m2 = 0;
+      top2_step<kDppQuadXor1>(m1, m2);
+      if (gsz >= 4) top2_step<kDppQuadXor2>(m1, m2);
+      if (gsz >= 8) top2_step<kDppHalfMirror>(m1, m2);
+      if (gsz >= 16) top2_step<kDppMirror>(m1, m2);
+      if (gsz >= 32) {
+        // rows (16 lanes) 0+1 and 2+3 (gsz 32), or all four (gsz 64)
+        uint32_t a1 = __builtin_amdgcn_readlane(m1, 0), a2 = __builtin_amdgcn_readlane(m2, 0);
+        uint32_t b1 = __builtin_amdgcn_readlane(m1, 32), b2 = __builtin_amdgcn_readlane(m2, 32);
+        top2_merge(a1, a2, __builtin_amdgcn_readlane(m1, 16), __builtin_amdgcn_readlane(m2, 16));
+        top2_merge(b1, b2, __builtin_amdgcn_readlane(m1, 48), __builtin_amdgcn_readlane(m2, 48));
+        if (gsz == 64) {
+          top2_merge(a1, a2, b1, b2);
+          b1 = a1;
+          b2 = a2;
+        }
+        m1 = lane < 32 ? a1 : b1;
+        m2 = lane < 32 ? a2 : b2;
+      }
+      const float gs = ordered_to_float(m1) + ordered_to_float(m2);
+      const float t = __shfl(gs, (lane % R) * gsz);
+      if (lane / R == j) my_gs = t;
+    }
+    // keep the topk_group groups of highest (score, lower index) key: a
+    // group is kept when fewer than topk_group keys beat it
+    const uint64_t gkey = lane < p.G ? rank_key(my_gs, lane) : 0;
+    int above = 0;
+    for (int g = 0; g < p.G; ++g) above += readlane_u64(gkey, g) > gkey ? 1 : 0;
+    kept = __ballot(lane < p.G && above < p.topk_group);
+  } else {
+    // group scores: best and second best key of each group (an equal value
+    // at another index counts as the second best)
+    float my_gs = 0.0f;
+    for (int g = 0; g < p.G; ++g) {
+      uint64_t b1 = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = j * MOE_WAVE + lane;
+        if (key[j] && e / gsz == g && key[j] > b1) b1 = key[j];
+      }
+      b1 = wave_max_u64(b1);
+      uint64_t b2 = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = j * MOE_WAVE + lane;
+        if (key[j] && e / gsz == g && key[j] != b1 && key[j] > b2) b2 = key[j];
+      }
+      b2 = wave_max_u64(b2);
+      const float v1 = ordered_to_float((uint32_t)(b1 >> 32));
+      const float v2 = ordered_to_float((uint32_t)(b2 >> 32));
+      const float gs = v1 + v2;
+      if (lane == g) my_gs = gs;
+    }
+    uint64_t gkey = lane < p.G ? rank_key(my_gs, lane) : 0;
+    for (int i = 0; i < p.topk_group; ++i) {
+      const uint64_t m = wave_max_u64(gkey);
+      const int g = key_expert(m);
+      kept |= 1ull << g;
+      if (lane == g) gkey = 0;
+    }
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
