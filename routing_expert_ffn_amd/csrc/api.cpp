@@ -154,7 +154,7 @@ Layout layout_of(const Dims& d) {
   size_t nsplit = 1;
   if (d.xdt == MOE_BF16 && d.T > 0) {
     int sps;
-    nsplit = (size_t)router_splits(d.T, d.H, &sps);
+    nsplit = (size_t)router_splits(d.T, d.H, d.E, &sps);
   }
   L.rpart = take(nsplit > 1 ? nsplit * T * E * 4 : 0);
   L.cand = take(d.capacity > 0 && !d.drop ? T * (size_t)d.n_allowed * 4 : 0);
@@ -241,7 +241,7 @@ hipError_t run_router(const Dims& d, RouterArgs a, const void* x, const void* w_
   if (a.logits_in) return timed(K_ROUTE_SELECT, s, [&] { return launch_route_select(a, s); });
   if (d.xdt != MOE_BF16) return timed(K_ROUTER, s, [&] { return launch_router(a, d.xdt, s); });
   int sps;
-  const int S = router_splits(d.T, d.H, &sps);
+  const int S = router_splits(d.T, d.H, d.E, &sps);
   float* lg = a.logits_out ? a.logits_out : at<float>(ws, L.logits);
   RouterGemmArgs g{};
   g.T = (int)d.T;

@@ -196,8 +196,9 @@ const char* kernel_name(int id);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 // Fused fp32 router (GEMM on fp32 MFMA + selection).
 hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s);
-// K slices of the bf16 router GEMM for T tokens (>= 1) and its launch.
-int router_splits(int64_t T, int H, int* sps);
+// K slices of the bf16 router GEMM for T tokens (>= 1) and E experts, and
+// its launch.
+int router_splits(int64_t T, int H, int E, int* sps);
 hipError_t launch_router_gemm(const RouterGemmArgs& a, hipStream_t s);
 // Selection from partial logits (a.part, a.nsplit) or from a.logits_in.
 hipError_t launch_route_select(const RouterArgs& a, hipStream_t s);

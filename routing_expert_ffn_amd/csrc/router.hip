@@ -450,6 +450,133 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterGemmArgs a) {
   }
 }
 
+// Router GEMM for large batches: 128 tokens x 128*NB experts per workgroup
+// (wave w: experts w*32*NB .., all 128 tokens, 4 x NB MFMA blocks), one
+// workgroup per compute unit.  x is the operand streamed from HBM, so it
+// gets the deeper pipeline: four x stages (copied three steps ahead) and
+// three weight stages (two steps ahead; the weights are re-read from L2),
+// 160 KB of LDS for NB = 2.
+constexpr int kRgTokens = 128, kRgAStages = 4, kRgBStages = 3;
+
+template <int NB>
+__global__ __launch_bounds__(256) void router_gemm_big_kernel(RouterGemmArgs a) {
+  constexpr int EP = 128 * NB;
+  constexpr int A_STAGE = kRgTokens * 128, B_STAGE = EP * 128;
+  constexpr int A_PER_WAVE = kRgTokens / 8 / 4, B_PER_WAVE = EP / 8 / 4;
+  constexpr int MB = kRgTokens / 32;
+  __shared__ __attribute__((aligned(1024))) char lds[kRgAStages * A_STAGE + kRgBStages * B_STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRgTokens;
+  const int nk = a.H / 64;
+  const int kb = blockIdx.y * a.sps, ke = min(nk, kb + a.sps);
+  const int lrow = lane >> 3;
+  const bf16* x = static_cast<const bf16*>(a.x);
+  const bf16* w = static_cast<const bf16*>(a.w);
+  uint32_t aoff[A_PER_WAVE], boff[B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < A_PER_WAVE; ++i) {
+    const int r = (wave * A_PER_WAVE + i) * 8 + lrow;
+    const int tok = min(t0 + r, a.T - 1);
+    aoff[i] = (uint32_t)tok * (uint32_t)a.H + ((lane & 7) ^ swz_of_row(r)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_PER_WAVE; ++i) {
+    const int r = (wave * B_PER_WAVE + i) * 8 + lrow;
+    const int e = min(r, a.E - 1);
+    boff[i] = (uint32_t)e * (uint32_t)a.H + ((lane & 7) ^ swz_of_row(r)) * 8;
+  }
+  char* const a_dst = lds + wave * A_PER_WAVE * 1024;
+  char* const b_dst = lds + kRgAStages * A_STAGE + wave * B_PER_WAVE * 1024;
+  // copies of iteration i (i may precede kb: the prologue): x of step i+3
+  // and weights of step i+2, each when inside the slice
+  auto issue = [&](int i) {
+    const int ka = i + 3, kw = i + 2;
+    if (ka < ke) {
+#pragma unroll
+      for (int q = 0; q < A_PER_WAVE; ++q) copy16(x + ka * 64 + aoff[q], a_dst + (ka % kRgAStages) * A_STAGE + q * 1024);
+    }
+    if (kw >= kb && kw < ke) {
+#pragma unroll
+      for (int q = 0; q < B_PER_WAVE; ++q) copy16(w + kw * 64 + boff[q], b_dst + (kw % kRgBStages) * B_STAGE + q * 1024);
+    }
+  };
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+  int slot[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) slot[kk] = ((kk * 2 + (lane >> 5)) ^ swz_of_row(lane & 15)) << 4;
+  const int arow = (lane & 31) * 128;
+  const int brow = (wave * 32 * NB + (lane & 31)) * 128;
+
+  for (int i = kb - 3; i < kb; ++i) issue(i);
+  for (int ks = kb; ks < ke; ++ks) {
+    // in issue order, the copies after the weights of step ks are x of step
+    // ks+2 and weights of step ks+1 (when inside the slice): wait until only
+    // those are in flight, so x and weights of step ks have landed; the
+    // barrier then also frees the stages read in step ks-1
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of step ks-1 are done
+    if (ks + 2 < ke)
+      wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
+    else if (ks + 1 < ke)
+      wait_vmem_upto<B_PER_WAVE>();
+    else
+      wait_vmem_upto<0>();
+    __builtin_amdgcn_s_barrier();
+    issue(ks);
+    const char* sa = lds + (ks % kRgAStages) * A_STAGE;
+    const char* sb = lds + kRgAStages * A_STAGE + (ks % kRgBStages) * B_STAGE;
+    // fragments of sub-step kk+1 are read while sub-step kk's MFMAs run
+    bf16x8 fa[2][MB], fb[2][NB];
+    auto read = [&](int kk, bf16x8(&ra)[MB], bf16x8(&rb)[NB]) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) ra[m] = *reinterpret_cast<const bf16x8*>(sa + arow + m * 32 * 128 + slot[kk]);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) rb[n] = *reinterpret_cast<const bf16x8*>(sb + brow + n * 32 * 128 + slot[kk]);
+    };
+    read(0, fa[0], fb[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) read(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][m], fb[kk & 1][n], acc[m][n], 0, 0, 0);
+      if (kk < 3) {
+        // one fragment read after each MFMA (left alone, the scheduler puts
+        // all reads first and waits for them)
+        constexpr int NR = MB + NB, NM = MB * NB;
+#pragma unroll
+        for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        }
+        if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+        if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  float* out = a.out + (int64_t)blockIdx.y * a.T * a.E;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int e = wave * 32 * NB + n * 32 + (lane & 31);
+    if (e >= a.E) continue;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = t0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (tok < a.T) out[(int64_t)tok * a.E + e] = acc[m][n][r];
+      }
+  }
+}
+
 // Selection: one wavefront per token.  The token's logits are the sum of its
 // nsplit partial rows (in slice order) plus logit_bias, or logits_in as
 // given; they are written to logits_out when set, kept in LDS, and routed.
@@ -837,23 +964,38 @@ hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s) {
   return dtype == 1 ? launch_router_d<bf16>(a, s) : launch_router_d<float>(a, s);
 }
 
-int router_splits(int64_t T, int H, int* sps) {
-  // enough (token tile, K slice) workgroups for two per compute unit (80 KB
-  // of LDS each): the GEMM streams x from HBM with one step of prefetch, so
-  // its speed is the bytes in flight per CU; 64-token tiles, K split into
-  // slices of whole 64-wide steps, at most 32 slices
+// Large batches (at least 64 tiles of 128 tokens, at most 256 experts) take
+// the 128-token kernel, one workgroup per compute unit.
+static bool router_big_tiles(int64_t T, int E) { return E <= 256 && (T + kRgTokens - 1) / kRgTokens >= 64; }
+
+int router_splits(int64_t T, int H, int E, int* sps) {
+  // enough (token tile, K slice) workgroups to fill the compute units: the
+  // GEMM streams x from HBM, so its speed is the bytes in flight per CU.
+  // 64-token tiles at two workgroups per CU (80 KB of LDS each, one step of
+  // prefetch), or 128-token tiles at one (three steps of x in flight); K is
+  // split into slices of whole 64-wide steps, at most 32 slices
   const int nk = H / 64;
-  const int64_t tiles = (T + 63) / 64;
+  const bool big = router_big_tiles(T, E);
+  const int64_t tiles = big ? (T + kRgTokens - 1) / kRgTokens : (T + 63) / 64;
+  const int64_t want = big ? 256 : 512;
   int S = 1;
-  if (tiles < 512) S = (int)std::min<int64_t>((512 + tiles - 1) / tiles, 32);
+  if (tiles < want) S = (int)std::min<int64_t>((want + tiles - 1) / tiles, 32);
   S = std::min(S, nk);
   const int per = (nk + S - 1) / S;
   *sps = per;
   return (nk + per - 1) / per;
 }
 
+template <int NB>
+hipError_t launch_router_gemm_big_t(const RouterGemmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.T + kRgTokens - 1) / kRgTokens), (unsigned)a.S);
+  hipLaunchKernelGGL((router_gemm_big_kernel<NB>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_gemm(const RouterGemmArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  if (router_big_tiles(a.T, a.E)) return a.E <= 128 ? launch_router_gemm_big_t<1>(a, s) : launch_router_gemm_big_t<2>(a, s);
   if (a.E <= 128) return launch_router_gemm_t<1>(a, s);
   if (a.E <= 256) return launch_router_gemm_t<2>(a, s);
   return launch_router_gemm_t<4>(a, s);

@@ -283,6 +283,37 @@ def test_combine_stage(dtype):
         assert np.all(np.abs(o - ref) <= tol)
 
 
+@pytest.mark.parametrize("T,H,E", [(8200, 7168, 256), (12811, 1024, 96), (16461, 1024, 200), (8200, 256, 64),
+                                   (8063, 2048, 256)])
+def test_router_gemm_large_batches(T, H, E):
+    """The router GEMM at large batch sizes (128-token tiles at one workgroup
+    per compute unit, K split into slices, ragged last token tile, ragged last
+    slice, slices of one step) and just below them (64-token tiles): logits of every token
+    of the first and last tiles and of a sample in between against the
+    oracle's dot products, and the routing of the GPU logits bit-exact."""
+    shape = TEST_SHAPES["v3_small"].with_(T=T, H=H, E=E, G=8 if E % 8 == 0 else 1,
+                                         topk_group=4 if E % 8 == 0 else 1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(T + H + E)
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((E, H), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
+    sb = (torch.rand((E,), generator=g, device="cuda") * 0.1 - 0.05).contiguous()
+    lo = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    idx, wts = moe.route(moe.make_config(shape), T, x=x, w_router=w, sel_bias=sb, logits_out=lo,
+                         expert_counts=counts)
+    torch.cuda.synchronize()
+    L = lo.cpu().numpy()
+    rng = np.random.default_rng(T)
+    tokens = np.unique(np.concatenate([np.arange(130), np.arange(T - 130, T), rng.choice(T, 60, replace=False)]))
+    ol = oracle.router_logits(shape, to_oracle(x[tokens]), to_oracle(w))
+    assert np.max(np.abs(L[tokens] - ol)) <= LOGIT_ATOL
+    oidx, ow, _, oc = oracle.select(shape, L, sb.cpu().numpy())
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    np.testing.assert_allclose(wts.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
+
+
 # ---- routing edge cases ------------------------------------------------------------
 
 def test_route_ties_and_sigmoid_near_ties_from_given_logits():
@@ -313,6 +344,34 @@ def test_route_ties_and_sigmoid_near_ties_from_given_logits():
     oidx2, ow2, _, _ = oracle.select(sm, L, None)
     assert np.array_equal(idx2.cpu().numpy(), oidx2)
     np.testing.assert_allclose(w2.cpu().numpy(), ow2, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("E,G,tg,k", [(64, 32, 4, 6), (128, 32, 8, 8), (256, 32, 4, 8), (256, 16, 3, 8),
+                                      (256, 8, 4, 8), (256, 4, 2, 8), (512, 8, 3, 8), (192, 3, 2, 6),
+                                      (160, 8, 3, 6), (96, 4, 2, 4)])
+def test_group_limit_every_group_size(E, G, tg, k):
+    """Group-limited sigmoid selection for groups of 2, 4, 8, 16, 32 and 64
+    experts (kept in place inside a register) and of 20 and 24 (the general
+    walk), bit-exact with the oracle on logits with exact ties and scores one
+    ulp apart."""
+    shape = TEST_SHAPES["v3_small"].with_(E=E, G=G, topk_group=tg, k=k)
+    T = 192
+    rng = np.random.default_rng(E * 100 + G)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[:24] = 0.5                                       # every score ties
+    base = np.float32(-0.2)
+    L[24:96] = base + np.spacing(base) * rng.integers(0, 4, (72, E)).astype(np.float32)
+    sb = (rng.uniform(-0.05, 0.05, E)).astype(np.float32)
+    sb[::4] = 0.0
+    cfg = moe.make_config(shape)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    idx, w = moe.route(cfg, T, logits_in=torch.from_numpy(L).cuda(), sel_bias=torch.from_numpy(sb).cuda(),
+                       expert_counts=counts)
+    torch.cuda.synchronize()
+    oidx, ow, _, oc = oracle.select(shape, L, sb)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
 
 
 def test_sqrtsoftplus_near_ties_from_given_logits():
