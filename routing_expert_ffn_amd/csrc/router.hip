@@ -276,6 +276,22 @@ __device__ __forceinline__ int token_topk(const RouteParams& p, uint64_t (&key)[
   return my_e;
 }
 
+// The value of lane ^ s (s < 64; s is a constant once the sort is
+// unrolled): DPP inside rows of 16 lanes for s <= 8 (row_ror:n gives lane i
+// the value of lane (i - n) mod 16, so s = 4 takes the rotations by 12 and by
+// 4 for the lanes below and above their partner, s = 8 the rotation by 8),
+// a bpermute across rows.
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int lane, int s) {
+  if (s == 1) return dpp_u64<kDppQuadXor1>(v);
+  if (s == 2) return dpp_u64<kDppQuadXor2>(v);
+  if (s == 4) {
+    const uint64_t up = dpp_u64<0x12C>(v), down = dpp_u64<0x124>(v);
+    return (lane & 4) ? down : up;
+  }
+  if (s == 8) return dpp_u64<0x128>(v);
+  return __shfl_xor(v, s);
+}
+
 // Descending bitonic sort of the 64*NJ keys of the wavefront; element
 // i = j*64 + lane ends holding rank i.
 template <int NJ>
@@ -293,7 +309,7 @@ __device__ __forceinline__ void wave_bitonic_desc(uint64_t (&key)[NJ], int lane)
         if (stride >= MOE_WAVE)
           other = key[j ^ (stride / MOE_WAVE)];
         else
-          other = __shfl_xor(key[j], stride);
+          other = lane_xor_u64(key[j], lane, stride);
         const bool lower = (i & stride) == 0;
         const bool desc = (i & size) == 0;
         const bool keep_max = lower == desc;
@@ -751,7 +767,20 @@ __global__ __launch_bounds__(kCapWaves * 64) void capacity_serial_kernel(Capacit
   for (int t0 = 0; t0 < p.T; t0 += chunk) {
     const int nt = min(chunk, p.T - t0);
     __syncthreads();  // previous chunk's gates are done with sel
-    for (int i = tid; i < nt * NA; i += kCapWaves * 64) cand[i] = a.cand[(int64_t)t0 * NA + i];
+    {
+      // eight loads in flight per thread (a load, then its LDS store, one
+      // at a time would put a memory round trip per element on the chain)
+      const int n = nt * NA;
+      const int32_t* src = a.cand + (int64_t)t0 * NA;
+      for (int i0 = tid; i0 < n; i0 += 8 * kCapWaves * 64) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[min(i0 + u * kCapWaves * 64, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * kCapWaves * 64 < n) cand[i0 + u * kCapWaves * 64] = v[u];
+      }
+    }
     __syncthreads();
     if (wave == 0) {
       // the first 64 ranked candidates of 8 tokens are read ahead into
