@@ -261,14 +261,17 @@ def test_expert_ffn_gathers_x_up_to_2gib():
     del x, y
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_combine_stage(dtype):
+@pytest.mark.parametrize("dtype,k,S", [("bf16", 4, 2), ("f32", 4, 2), ("bf16", 12, 1), ("bf16", 32, 0),
+                                       ("f32", 9, 3)])
+def test_combine_stage(dtype, k, S):
+    """Combine of expert rows: slots in batches of eight (k up to 32, a
+    partial last batch), empty slots, zero to three shared experts."""
     from workloads import LayerShape
     H = 256 if dtype == "bf16" else 64
-    shape = LayerShape("c", T=300, H=H, E=16, S=2, k=4, I=128, dtype=dtype)
-    rng = np.random.default_rng(4)
-    T, k, S = shape.T, shape.k, shape.S
-    idx = np.stack([rng.permutation(16)[:k] for _ in range(T)]).astype(np.int32)
+    shape = LayerShape("c", T=300, H=H, E=40, S=S, k=k, I=128, dtype=dtype)
+    rng = np.random.default_rng(4 + k)
+    T = shape.T
+    idx = np.stack([rng.permutation(40)[:k] for _ in range(T)]).astype(np.int32)
     idx[rng.random((T, k)) < 0.1] = -1
     _, _, _, slot_row = oracle.permute(shape, idx)
     w = rng.random((T, k)).astype(np.float32)
@@ -281,6 +284,20 @@ def test_combine_stage(dtype):
         o = out.float().cpu().numpy()
         tol = 1e-5 + (bf16_half_ulp(ref) if out_dtype == "bf16" else 1e-6 * np.abs(ref))
         assert np.all(np.abs(o - ref) <= tol)
+
+
+@pytest.mark.parametrize("E,G,tg,k", [(512, 8, 4, 32), (384, 1, 1, 12)])
+def test_layer_many_experts_and_slots(E, G, tg, k):
+    """Whole layer with more than 256 routed experts (router GEMM over four
+    expert blocks per wavefront, eight experts per lane in the selection) and
+    up to 32 slots per token (the combine's slot batches), every token
+    against the oracle."""
+    shape = TEST_SHAPES["v3_small"].with_(T=203, E=E, G=G, topk_group=tg, k=k)
+    inp = make_inputs(shape, device="cuda")
+    for out_dtype in ("f32", "bf16"):
+        g = run_layer(shape, inp, out_dtype)
+        err, excluded = check_layer(shape, inp, g, np.arange(shape.T), out_dtype)
+        print("E=%d k=%d out=%s: max err %.3g x RMS, %d tokens below the margin" % (E, k, out_dtype, err, excluded))
 
 
 @pytest.mark.parametrize("T,H,E", [(8200, 7168, 256), (12811, 1024, 96), (16461, 1024, 200), (8200, 256, 64),
