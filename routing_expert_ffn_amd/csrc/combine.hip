@@ -2,8 +2,8 @@
 //   out[t] = sum_j w[t,j] * y_routed[slot_row[t,j]] + sum_s y_shared[s*T + t]
 // ("15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the
 // router sketch's last line: weighted routed experts plus the shared expert).
-// One workgroup per token (one thread per 8 values of the row); 16-byte loads
-// of the expert rows (routed rows fp32 or bf16, shared rows fp32), fp32
+// One workgroup per token (one thread per 8 values of the row); 16-byte
+// non-temporal loads (every expert row is read exactly once) of the expert rows (routed rows fp32 or bf16, shared rows fp32), fp32
 // accumulation in a fixed order (slots, then shared experts), so the result
 // is deterministic.
 #include <algorithm>
@@ -22,7 +22,9 @@ struct Vec8<bf16> {
   struct Raw {
     bf16x8 x;
   };
-  static __device__ __forceinline__ Raw load_raw(const bf16* p) { return Raw{*reinterpret_cast<const bf16x8*>(p)}; }
+  static __device__ __forceinline__ Raw load_raw(const bf16* p) {
+    return Raw{__builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p))};
+  }
   static __device__ __forceinline__ float at(const Raw& r, int i) { return (float)r.x[i]; }
   static __device__ __forceinline__ void load(const bf16* p, float (&v)[8]) {
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
@@ -42,7 +44,8 @@ struct Vec8<float> {
     f32x4 a, b;
   };
   static __device__ __forceinline__ Raw load_raw(const float* p) {
-    return Raw{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+    return Raw{__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
+               __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4))};
   }
   static __device__ __forceinline__ float at(const Raw& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
   static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
