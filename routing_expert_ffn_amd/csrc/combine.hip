@@ -3,9 +3,9 @@
 // ("15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the
 // router sketch's last line: weighted routed experts plus the shared expert).
 // One workgroup per token (one thread per 8 values of the row); 16-byte
-// non-temporal loads (every expert row is read exactly once) of the expert rows (routed rows fp32 or bf16, shared rows fp32), fp32
-// accumulation in a fixed order (slots, then shared experts), so the result
-// is deterministic.
+// non-temporal loads of the expert rows (each is read exactly once; routed
+// rows fp32 or bf16, shared rows fp32), fp32 accumulation in a fixed order
+// (slots, then shared experts), so the result is deterministic.
 #include <algorithm>
 
 #include "common.hpp"
