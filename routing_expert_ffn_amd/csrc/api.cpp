@@ -483,6 +483,10 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   // bf16 and FP8 kernels share each GEMM's last items between the XCDs
   // (the fp32 kernel has no LDS to broadcast the counter)
   g.pool = d.dtype != MOE_F32 ? sa.pool : nullptr;
+  // at most BM tokens: every expert segment (a token takes an expert at most
+  // once; the shared experts have T rows) fits in one row tile, so each
+  // weight tile is read by a single item and streams past the caches
+  g.stream_b = d.T <= BM ? 1 : 0;
   void* h = at<void>(ws, L.h);
   // gate/up + SwiGLU
   g.K = d.H;

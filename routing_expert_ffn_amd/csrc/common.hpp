@@ -155,6 +155,12 @@ __device__ __forceinline__ void copy16(const bf16* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
 }
 
+// copy16 with the non-temporal cache policy, for data read exactly once (the
+// expert weights when every expert has at most one row tile).
+__device__ __forceinline__ void copy16_nt(const bf16* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 2);
+}
+
 // Raw buffer resource over [base, base + bytes), bytes < 2^31: a buffer load
 // whose offset lies past the end returns zeros and touches no memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {

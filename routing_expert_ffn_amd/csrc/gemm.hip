@@ -45,12 +45,17 @@ constexpr int kEpWave = kWM * (128 * 2 + 16);
 static_assert(4 * kEpWave <= kLdsBytes, "epilogue staging fits in the stages");
 
 // Copies I0 .. I0+N-1 of a wave's group: copy i reads base + off[i] and
-// fills the 1 KB of LDS at dst + i*1024.
-template <int I0, int N, int M>
+// fills the 1 KB of LDS at dst + i*1024 (NT: non-temporal).
+template <bool NT, int I0, int N, int M>
 __device__ __forceinline__ void copy_rows(const bf16* base, const uint32_t (&off)[M], char* dst) {
   static_assert(I0 + N <= M, "copy range");
 #pragma unroll
-  for (int i = I0; i < I0 + N; ++i) copy16(base + off[i], dst + i * 1024);
+  for (int i = I0; i < I0 + N; ++i) {
+    if constexpr (NT)
+      copy16_nt(base + off[i], dst + i * 1024);
+    else
+      copy16(base + off[i], dst + i * 1024);
+  }
 }
 
 // The same through a buffer resource: copy i reads byte voff[i] + soff
@@ -121,7 +126,7 @@ __device__ __forceinline__ void interleave_reads() {
 // expert's last row tile 3*kWM/4 when it has at most 3*kWM/2 rows and kWM/2
 // when it has at most kWM, which then costs three quarters or half of the
 // MFMAs instead of computing padding.
-template <int WM, bool GATEUP>
+template <int WM, bool GATEUP, bool NTB>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, int nt, int row0, int rows) {
   constexpr int BM = 2 * WM;
   constexpr int MB = WM / 32;
@@ -206,8 +211,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   // step before its A; indices clamped to the last step: a re-copy lands in
   // a stage that is not read again), then wait for step 0
   copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, 0, a_dst);
-  copy_rows<0, B_PER_WAVE>(bbase, boff, b_dst);
-  copy_rows<0, B_PER_WAVE>(bbase + min(1, nk - 1) * kBK, boff, b_dst + kBStage);
+  copy_rows<NTB, 0, B_PER_WAVE>(bbase, boff, b_dst);
+  copy_rows<NTB, 0, B_PER_WAVE>(bbase + min(1, nk - 1) * kBK, boff, b_dst + kBStage);
   copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, min(1, nk - 1) * kRowBytes, a_dst + kAStage);
   wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
   __builtin_amdgcn_s_barrier();
@@ -224,15 +229,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
     // sub-steps 0, 1 and 2: B of step kt+2 (3 + 3 + 2 copies) into the stage
     // freed at the last barrier
     load_frags<MB>(sa, sb, arow, brow, slot[1], fa1, fb1);
-    copy_rows<0, BH>(bn, boff, b_dst + sbf * kBStage);
+    copy_rows<NTB, 0, BH>(bn, boff, b_dst + sbf * kBStage);
     mfma_step<MB>(fa0, fb0, acc);
     interleave_reads<MB, BH>();
     load_frags<MB>(sa, sb, arow, brow, slot[2], fa0, fb0);
-    copy_rows<BH, BH>(bn, boff, b_dst + sbf * kBStage);
+    copy_rows<NTB, BH, BH>(bn, boff, b_dst + sbf * kBStage);
     mfma_step<MB>(fa1, fb1, acc);
     interleave_reads<MB, BH>();
     load_frags<MB>(sa, sb, arow, brow, slot[3], fa1, fb1);
-    copy_rows<BH2, B_PER_WAVE - BH2>(bn, boff, b_dst + sbf * kBStage);
+    copy_rows<NTB, BH2, B_PER_WAVE - BH2>(bn, boff, b_dst + sbf * kBStage);
     mfma_step<MB>(fa0, fb0, acc);
     interleave_reads<MB, B_PER_WAVE - BH2>();
     // this wave's reads of the current stages are done and A and B of step
@@ -322,7 +327,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   }
 }
 
-template <bool GATEUP>
+// NTB: the weights are read with the non-temporal policy (each is read once).
+template <bool GATEUP, bool NTB>
 __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   Work w;
@@ -331,14 +337,14 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
     // an expert's last row tile of 129-192 rows runs three 32-row blocks per
     // wavefront instead of four (a quarter less MFMA work on padding rows)
     if (w.rows > 3 * kWM / 2)
-      gemm_tile<kWM, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile<kWM, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
     else
-      gemm_tile<3 * kWM / 4, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile<3 * kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
   } else {
-    gemm_tile<kWM / 2, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+    gemm_tile<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();  // every wave is past its last reads of the LDS stages
-      gemm_tile<kWM / 2, GATEUP>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+      gemm_tile<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
     }
   }
 }
@@ -458,10 +464,13 @@ hipError_t launch_gateup(const GemmArgs& a, int dtype, int64_t mtile_bound, hipS
   if (dtype == 2) return launch_gateup_fp8(a, mtile_bound, s);
   const int64_t grid = mtile_bound * a.n_tiles;
   if (grid <= 0) return hipSuccess;
-  if (dtype == 1)
-    hipLaunchKernelGGL((expert_gemm_bf16<true>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
+  if (dtype != 1) {
     hipLaunchKernelGGL((expert_gemm_f32<true>), dim3((unsigned)grid), dim3(64), 0, s, a);
+  } else if (a.stream_b) {
+    hipLaunchKernelGGL((expert_gemm_bf16<true, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((expert_gemm_bf16<true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -469,9 +478,12 @@ hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStr
   if (dtype == 2) return launch_down_fp8(a, mtile_bound, s);
   const int64_t grid = mtile_bound * a.n_tiles;
   if (grid <= 0) return hipSuccess;
-  if (dtype == 1)
-    hipLaunchKernelGGL((expert_gemm_bf16<false>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
+  if (dtype != 1) {
     hipLaunchKernelGGL((expert_gemm_f32<false>), dim3((unsigned)grid), dim3(64), 0, s, a);
+  } else if (a.stream_b) {
+    hipLaunchKernelGGL((expert_gemm_bf16<false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((expert_gemm_bf16<false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }

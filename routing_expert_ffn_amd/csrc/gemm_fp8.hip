@@ -70,12 +70,17 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
 }
 
 // Copies I0 .. I0+N-1 of a wave's group: copy i reads base + off[i] (bytes)
-// and fills the 1 KB of LDS at dst + i*1024.
-template <int I0, int N, int M>
+// and fills the 1 KB of LDS at dst + i*1024 (NT: non-temporal).
+template <bool NT, int I0, int N, int M>
 __device__ __forceinline__ void copy_rows8(const uint8_t* base, const uint32_t (&off)[M], char* dst) {
   static_assert(I0 + N <= M, "copy range");
 #pragma unroll
-  for (int i = I0; i < I0 + N; ++i) copy16(reinterpret_cast<const bf16*>(base + off[i]), dst + i * 1024);
+  for (int i = I0; i < I0 + N; ++i) {
+    if constexpr (NT)
+      copy16_nt(reinterpret_cast<const bf16*>(base + off[i]), dst + i * 1024);
+    else
+      copy16(reinterpret_cast<const bf16*>(base + off[i]), dst + i * 1024);
+  }
 }
 
 // The same through a buffer resource: copy i reads byte voff[i] + soff
@@ -176,7 +181,7 @@ __device__ __forceinline__ void step_scales(const uint32_t (&ga)[MB], uint32_t g
   sb[2] = sb[3] = (int)(gb1 >> sh);
 }
 
-template <int WM, bool GATEUP>
+template <int WM, bool GATEUP, bool NTB>
 __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int e, int nt, int row0, int rows) {
   constexpr int BM = 2 * WM;
   constexpr int MB = WM / 32;
@@ -266,8 +271,8 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   // prologue: A and B of steps 0 and 1 in the order of the main loop (B of a
   // step before its A), then wait for step 0
   copy_rows8_buf<0, A_PER_WAVE>(arsrc, aoff, 0, a_dst);
-  copy_rows8<0, B_PER_WAVE>(bbase, boff, b_dst);
-  copy_rows8<0, B_PER_WAVE>(bbase + min(1, nk - 1) * kRowBytes, boff, b_dst + kBStage);
+  copy_rows8<NTB, 0, B_PER_WAVE>(bbase, boff, b_dst);
+  copy_rows8<NTB, 0, B_PER_WAVE>(bbase + min(1, nk - 1) * kRowBytes, boff, b_dst + kBStage);
   copy_rows8_buf<0, A_PER_WAVE>(arsrc, aoff, min(1, nk - 1) * kRowBytes, a_dst + kAStage);
   wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
   __builtin_amdgcn_s_barrier();
@@ -295,7 +300,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
     step_scales<MB>(ga, gb0, gb1, (kt & 3) * 8, sa_k, sb_k);
     // sub-step 0: B of step kt+2 into the stage freed at the last barrier
     load_frags8<MB>(sa, sb, arow, brow, s10, s11, fa1, fb1);
-    copy_rows8<0, B_PER_WAVE>(bbase + min(kt + 2, nk - 1) * kRowBytes, boff, b_dst + sbf * kBStage);
+    copy_rows8<NTB, 0, B_PER_WAVE>(bbase + min(kt + 2, nk - 1) * kRowBytes, boff, b_dst + sbf * kBStage);
     mfma_step8<MB>(fa0, fb0, sa_k, sb_k, acc);
     interleave8<MB, B_PER_WAVE>();
     // the wave's reads of the current stages are done and A and B of step
@@ -428,7 +433,8 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   }
 }
 
-template <bool GATEUP>
+// NTB: the weights are read with the non-temporal policy (each is read once).
+template <bool GATEUP, bool NTB>
 __global__ __launch_bounds__(256, 1) void expert_gemm_fp8(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   Work w;
@@ -436,14 +442,14 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_fp8(GemmArgs a) {
   if (!w.pair) {
     // a last row tile of 129-192 rows: three 32-row blocks per wavefront
     if (w.rows > 3 * kWM / 2)
-      gemm_tile_fp8<kWM, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile_fp8<kWM, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
     else
-      gemm_tile_fp8<3 * kWM / 4, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile_fp8<3 * kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
   } else {
-    gemm_tile_fp8<kWM / 2, GATEUP>(a, lds, w.e, w.nt, w.row0, w.rows);
+    gemm_tile_fp8<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();
-      gemm_tile_fp8<kWM / 2, GATEUP>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+      gemm_tile_fp8<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
     }
   }
 }
@@ -523,14 +529,22 @@ hipError_t launch_row_scales(const RowScaleArgs& a, hipStream_t s) {
 hipError_t launch_gateup_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s) {
   const int64_t grid = mtile_bound * a.n_tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((expert_gemm_fp8<true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  if (a.stream_b) {
+    hipLaunchKernelGGL((expert_gemm_fp8<true, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((expert_gemm_fp8<true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_down_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s) {
   const int64_t grid = mtile_bound * a.n_tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((expert_gemm_fp8<false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  if (a.stream_b) {
+    hipLaunchKernelGGL((expert_gemm_fp8<false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((expert_gemm_fp8<false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

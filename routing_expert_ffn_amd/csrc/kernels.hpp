@@ -122,6 +122,9 @@ struct GemmArgs {
   // range, taken by whichever XCD gets there first), zeroed before the
   // launch; null: every item stays with its XCD
   int32_t* pool;
+  // 1: every expert has at most one row tile, so each weight tile is read by
+  // one item only and the weight copies take the non-temporal policy
+  int stream_b;
 };
 
 // Weight scales repacked with rows padded to 4 bytes (three matrices).
