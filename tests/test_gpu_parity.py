@@ -223,6 +223,38 @@ def test_expert_ffn_stage_rows():
         assert err <= 2e-2 * rms + np.max(bf16_half_ulp(ref)), (e, err / rms)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_weight_stream_policy_is_bit_identical(fp8):
+    """At most 256 tokens the expert GEMMs copy the weights with the
+    non-temporal cache policy, above that with the default one; a cache hint
+    only, so the rows of 256 tokens come out bit-identical when a 257th token
+    is appended (its rows go to the end of every expert segment, the earlier
+    rows keep their row tiles and their K order)."""
+    base = TEST_SHAPES["v3_fp8_small" if fp8 else "v3_small"]
+    shape = base.with_(T=257)
+    inp = make_inputs(shape, device="cuda")
+    rng = np.random.default_rng(11)
+    idx_all = np.stack([rng.permutation(shape.E)[:shape.k] for _ in range(257)]).astype(np.int32)
+    ys, srs = [], []
+    for T in (256, 257):
+        cfg = moe.make_config(shape.with_(T=T))
+        x = inp["x"][:T].contiguous()
+        _, offsets, row_token, slot_row = moe.permute(cfg, torch.from_numpy(idx_all[:T]).cuda())
+        if fp8:
+            y = moe.expert_ffn_fp8(cfg, x, inp["w_gate"], inp["s_gate"], inp["w_up"], inp["s_up"], inp["w_down"],
+                                   inp["s_down"], offsets, row_token)
+        else:
+            y = moe.expert_ffn(cfg, x, inp["w_gate"], inp["w_up"], inp["w_down"], offsets, row_token)
+        torch.cuda.synchronize()
+        ys.append(y.float().cpu().numpy())
+        srs.append(slot_row.cpu().numpy())
+    k = shape.k
+    a = ys[0][srs[0][:256].ravel()]
+    b = ys[1][srs[1][:256].ravel()]
+    assert np.array_equal(a, b)
+    assert np.array_equal(ys[0][256 * k:256 * k + 256], ys[1][257 * k:257 * k + 256])   # shared expert rows
+
+
 def test_expert_ffn_gathers_x_up_to_2gib():
     """The gate/up GEMM gathers token rows through one 32-bit buffer resource
     over x: with x just under 2 GiB (149796 tokens of H = 7168), the rows of
