@@ -469,7 +469,8 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterGemmArgs a) {
 // Router GEMM for large batches: 128 tokens x 128*NB experts per workgroup
 // (wave w: experts w*32*NB .., all 128 tokens, 4 x NB MFMA blocks), one
 // workgroup per compute unit.  x is the operand streamed from HBM, so it
-// gets the deeper pipeline: four x stages (copied three steps ahead) and
+// gets the deeper pipeline (and the non-temporal policy: each x byte is
+// read by one workgroup): four x stages (copied three steps ahead) and
 // three weight stages (two steps ahead; the weights are re-read from L2),
 // 160 KB of LDS for NB = 2.
 constexpr int kRgTokens = 128, kRgAStages = 4, kRgBStages = 3;
@@ -509,7 +510,8 @@ __global__ __launch_bounds__(256) void router_gemm_big_kernel(RouterGemmArgs a) 
     const int ka = i + 3, kw = i + 2;
     if (ka < ke) {
 #pragma unroll
-      for (int q = 0; q < A_PER_WAVE; ++q) copy16(x + ka * 64 + aoff[q], a_dst + (ka % kRgAStages) * A_STAGE + q * 1024);
+      for (int q = 0; q < A_PER_WAVE; ++q)
+        copy16_nt(x + ka * 64 + aoff[q], a_dst + (ka % kRgAStages) * A_STAGE + q * 1024);
     }
     if (kw >= kb && kw < ke) {
 #pragma unroll
