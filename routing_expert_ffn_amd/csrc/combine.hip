@@ -4,8 +4,10 @@
 // router sketch's last line: weighted routed experts plus the shared expert).
 // One workgroup per token (one thread per 8 values of the row); 16-byte
 // non-temporal loads of the expert rows (each is read exactly once; routed
-// rows fp32 or bf16, shared rows fp32), fp32 accumulation in a fixed order
-// (slots, then shared experts), so the result is deterministic.
+// rows fp32 or bf16, shared rows fp32) and non-temporal stores of the output
+// (hundreds of MB at prefill sizes, more than the caches hold), fp32
+// accumulation in a fixed order (slots, then shared experts), so the result
+// is deterministic.
 #include <algorithm>
 
 #include "common.hpp"
@@ -35,7 +37,7 @@ struct Vec8<bf16> {
     bf16x8 x;
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = (bf16)v[i];
-    *reinterpret_cast<bf16x8*>(p) = x;
+    __builtin_nontemporal_store(x, reinterpret_cast<bf16x8*>(p));
   }
 };
 template <>
@@ -64,8 +66,8 @@ struct Vec8<float> {
       a[i] = v[i];
       b[i] = v[i + 4];
     }
-    *reinterpret_cast<f32x4*>(p) = a;
-    *reinterpret_cast<f32x4*>(p + 4) = b;
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
   }
 };
 
