@@ -95,7 +95,8 @@ typedef struct moe_config {
   int32_t scoring;               /* moe_scoring                                   */
   int32_t norm_topk_prob;        /* 1: gates renormalised over the selection     */
   float routed_scaling_factor;   /* multiplies every routed gate (2.5 for V3)    */
-  float capacity_factor;         /* <= 0: unlimited; else C = ceil(cf*T*k/E)    */
+  double capacity_factor;        /* <= 0: unlimited; else C = ceil(((cf*T)*k)/E)
+                                    evaluated in IEEE double, left to right      */
   int32_t dtype;                 /* moe_dtype of x and every weight (MOE_FP8: see
                                     moe_dtype)                                    */
   int32_t out_dtype;             /* moe_dtype of `out`                            */
@@ -168,14 +169,20 @@ moe_status moe_route_hash(const moe_config* cfg, int64_t T, const void* x, const
                           const int32_t* tid2eid, int64_t vocab, int32_t* topk_idx, float* topk_w,
                           int32_t* expert_counts, void* ws, size_t ws_bytes, void* stream);
 
-/* Dispatch: expert histogram and stable permutation of (token, slot) pairs.
+/* Dispatch: expert histogram and stable permutation of (token, slot) pairs
+ * ("MoE架构揭秘：大模型参数激活率与专家路由机制解析", section 4.1: the tokens of
+ * each expert are gathered together rather than masked per expert; "GPT-4 Has
+ * 1.8 Trillion Parameters. It Uses 2% of Them Per Token", section 4.2: the
+ * router's output is packed with the token ids into one routing batch that a
+ * single kernel dispatches to the experts).
  *   topk_idx       [T,k] int32, each row distinct experts in [0,E) or -1
  *   expert_counts  [E]   int32 out
  *   expert_offsets [E+1] int32 out: exclusive prefix sum of the counts
  *   row_token      [T*k + S*T] int32 out: token of every row (-1 = unused row)
  *   slot_row       [T,k] int32 out: row of (t, j), -1 for an empty slot
  * Rows of one expert are in ascending token order.  Out-of-range indices are
- * the caller's contract violation: they are counted nowhere (undefined rows). */
+ * the caller's contract violation: they are counted nowhere (undefined rows).
+ * T == 0: expert_counts and expert_offsets are set to zero (no rows). */
 moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx, int32_t* expert_counts,
                        int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row, void* ws,
                        size_t ws_bytes, void* stream);
@@ -193,13 +200,21 @@ moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const
                           const void* w_up, const void* w_down, const int32_t* expert_offsets,
                           const int32_t* row_token, void* y_rows, void* ws, size_t ws_bytes, void* stream);
 
-/* Combine: out[t] = sum_j topk_w[t,j] * y_rows[slot_row[t,j]] (empty slots
+/* Combine ("15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选
+ * 8 个", last line of its router code block: the layer output is the
+ * gate-weighted sum of the chosen experts' outputs plus the shared expert's):
+ * out[t] = sum_j topk_w[t,j] * y_rows[slot_row[t,j]] (empty slots
  * skipped) + sum_s y_rows[T*k + s*T + t], accumulated in fp32 in that order.
  *   y_rows [T*k+S*T, H] fp32; slot_row, topk_w [T,k]; out [T,H] out_dtype */
 moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, const int32_t* slot_row,
                        const float* topk_w, void* out, void* stream);
 
-/* The whole layer in one call: route, permute, experts and combine.
+/* The whole layer in one call: route, permute, experts and combine (the
+ * layer of "15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选
+ * 8 个", router code block from the logits to its last line, with the softmax
+ * routing of "MoE架构揭秘：大模型参数激活率与专家路由机制解析", section 3.1, and the
+ * capacity of "GPT-4 Has 1.8 Trillion Parameters ...", section 2.2, as
+ * configured).
  * out [T,H] in cfg->out_dtype.  topk_idx, topk_w, expert_counts and
  * logits_out are optional outputs (NULL = keep them in the workspace). */
 moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
@@ -255,7 +270,7 @@ moe_status moe_quantize_fp8(int64_t rows, int32_t K, const void* in, uint8_t* co
 /* One step of auxiliary-loss-free load balancing ("15. DeepSeek：MLA、MoE 与
  * MTP", section "V3 的 MoE：256 个专家怎样选 8 个", the bias paragraph) and the
  * load telemetry of its monitoring paragraph (plus the expert-call entropy of
- * "GPT-4 Has 1.8 Trillion Parameters ...", section 4.4).
+ * "GPT-4稀疏激活原理：2%参数调用背后的MoE工程实践", section 4.4).
  *   expert_counts [E] int32, e.g. from moe_route / moe_forward (N = their sum)
  *   sel_bias      [E] fp32, updated in place, or NULL (telemetry only): an
  *                 expert with n_e > N/E gets fl32(b - gamma), one with

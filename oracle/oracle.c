@@ -588,7 +588,7 @@ int oracle_combine(const oracle_layer* L, int64_t T, const double* y_rows, const
  * b <- fl32(b - gamma) or fl32(b + gamma).  The mean test is exact integer
  * arithmetic: n_e > N/E  <=>  n_e * E > N.
  * Load telemetry (the same section's monitoring paragraph; the expert-call
- * entropy of "GPT-4 Has 1.8 Trillion Parameters ...", section 4.4):
+ * entropy of "GPT-4稀疏激活原理：2%参数调用背后的MoE工程实践", section 4.4):
  * share[e] = n_e / N, stats = {entropy -sum share*ln(share) in nats (0*ln 0 =
  * 0), largest share, experts above the mean, experts below the mean}.  N == 0:
  * no update, shares 0, entropy 0. */

@@ -37,7 +37,7 @@ class moe_config(ctypes.Structure):
                 ("n_shared_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("moe_intermediate_size", ctypes.c_int32),
                 ("scoring", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
-                ("routed_scaling_factor", ctypes.c_float), ("capacity_factor", ctypes.c_float),
+                ("routed_scaling_factor", ctypes.c_float), ("capacity_factor", ctypes.c_double),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("drop_tokens", ctypes.c_int32)]
 
 

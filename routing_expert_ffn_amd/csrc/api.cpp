@@ -114,9 +114,11 @@ moe_status check_config(const moe_config* c, int64_t T, Dims& d) {
   if (c->drop_tokens != 0 && c->drop_tokens != 1) return fail(MOE_ERR_INVALID_ARG, "drop_tokens must be 0 or 1");
   d.drop = c->drop_tokens;
   d.capacity = 0;
-  if (c->capacity_factor > 0.0f) {
-    // C = ceil(((cf*T)*k)/E) evaluated in IEEE double, left to right
-    const double cap = std::ceil((double)c->capacity_factor * (double)T * (double)d.k / (double)d.E);
+  if (c->capacity_factor > 0.0) {
+    // C = ceil(((cf*T)*k)/E) evaluated in IEEE double, left to right, on the
+    // caller's double factor (a decimal such as 1.2 is not representable in
+    // fp32, and its fp32 value can make C one larger)
+    const double cap = std::ceil(c->capacity_factor * (double)T * (double)d.k / (double)d.E);
     if (cap > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "capacity too large");
     d.capacity = (int)cap;
     if (d.capacity < 1 && T > 0) d.capacity = 1;

@@ -5,8 +5,8 @@
 // than the mean has its selection-only bias lowered by gamma and one that
 // received fewer has it raised (an expert exactly at the mean keeps it); the
 // monitoring paragraph of the same section and the expert-call entropy of
-// "GPT-4 Has 1.8 Trillion Parameters. It Uses 2% of Them Per Token",
-// section 4.4, are the telemetry.  One workgroup, one thread per expert; the
+// "GPT-4稀疏激活原理：2%参数调用背后的MoE工程实践", section 4.4, are the
+// telemetry.  One workgroup, one thread per expert; the
 // mean test is exact integer arithmetic and the reductions run in a fixed
 // order, so the result is deterministic.
 #include "common.hpp"

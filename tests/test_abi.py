@@ -37,6 +37,24 @@ def test_library_exports_every_declared_function():
     assert set(moe.EXPORTS) <= exported
 
 
+def test_config_struct_layout_matches_the_header(tmp_path):
+    """The binding's moe_config has the size and field offsets the C compiler
+    gives the header's struct (capacity_factor is a double: 8-byte aligned)."""
+    fields = [f[0] for f in moe.moe_config._fields_]
+    prog = tmp_path / "layout.c"
+    prog.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\nint main(void){\n'
+                    '  printf("size %zu\\n", sizeof(moe_config));\n' +
+                    "".join('  printf("%s %%zu\\n", offsetof(moe_config, %s));\n' % (f, f) for f in fields) +
+                    "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)])
+    got = dict(line.split() for line in subprocess.check_output([str(exe)], text=True).splitlines())
+    assert int(got["size"]) == ctypes.sizeof(moe.moe_config)
+    for f in fields:
+        assert int(got[f]) == getattr(moe.moe_config, f).offset, f
+    assert moe.moe_config.capacity_factor.size == 8
+
+
 def test_version_and_clean_error_state():
     assert "gfx950" in moe.version()
 

@@ -110,15 +110,22 @@ def _exact_inputs(shape, inp, seed, large_gate=False):
     inp["x"] = torch.from_numpy(xv).to(torch.bfloat16).cuda()
 
 
+# Expert rows of exact-arithmetic inputs with large gate values: g and u are
+# exact, silu(g) = g, so h and its E4M3 codes are the same on both sides;
+# what remains is the fp32 rounding of the down projection's block sums.
+EXACT_REL = 2e-4
+
+
 def test_expert_stage_exact_arithmetic():
     """Codes and scales chosen so that every product and partial sum is exact
-    in the matrix cores: the expert rows then match the oracle to rounding,
-    on full and half-height row tiles and the shared expert."""
+    in the matrix cores and h is the same value on both sides: the expert rows
+    then match the oracle to rounding (within 2e-4 x RMS), on full and
+    half-height row tiles and the shared expert."""
     shape = TEST_SHAPES["v3_fp8_small"].with_(T=600)
     inp = make_inputs(shape, device="cuda")
     E = shape.E
     T = shape.T
-    _exact_inputs(shape, inp, 9)
+    _exact_inputs(shape, inp, 9, large_gate=True)
     idx = _routing(shape, 3)
     y, off, rt = _stage(shape, inp, idx)
     for e in (7, int(idx[100, 1]), E):
@@ -127,7 +134,7 @@ def test_expert_stage_exact_arithmetic():
         rms = np.sqrt(np.mean(ref ** 2))
         err = np.abs(y[rows] - ref) / rms
         print("expert %d: %d rows, max err %.3g x RMS" % (e, len(rows), err.max()))
-        assert err.max() <= 1e-3
+        assert err.max() <= EXACT_REL
 
 
 def test_h_codes_are_valid_roundings():
@@ -222,4 +229,4 @@ def test_expert_stage_row_tile_boundaries():
         ref = _oracle_rows(shape, inp, e, rt[rows].astype(np.int64))
         rms = np.sqrt(np.mean(ref ** 2))
         err = np.abs(y[rows] - ref) / rms
-        assert err.max() <= 1e-3, (e, counts[e] if e < E else T, err.max())
+        assert err.max() <= EXACT_REL, (e, counts[e] if e < E else T, err.max())

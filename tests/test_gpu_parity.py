@@ -14,7 +14,10 @@ Bars (FP8 experts: see check_layer):
 Capacity layers couple tokens through the expert counts, so their indices are
 compared in identical-logits mode (GPU logits fed to the oracle).
 """
+import ctypes
+import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -541,6 +544,46 @@ def test_capacity_rounds_match_oracle(T, cf, G):
     assert oc.max() == oracle.capacity(shape, T) or cf >= 2.0
 
 
+@pytest.mark.parametrize("cf,T,k,E", [(1.2, 160, 8, 256), (1.1, 320, 8, 256), (0.3, 320, 8, 256), (1.2, 40, 2, 8)])
+@pytest.mark.parametrize("drop", [False, True])
+@pytest.mark.parametrize("ranking", ["shared", "skewed"])
+def test_capacity_value_for_decimal_factors(cf, T, k, E, drop, ranking):
+    """Capacity factors that fp32 cannot represent (1.2 is the GPT-4 page's
+    configured value) give the same C on the library and the oracle: C =
+    ceil(((cf*T)*k)/E) in IEEE double.  At these sizes cf*T*k/E is an
+    integer in decimal, where an fp32 factor would make C one larger.  With
+    every token ranking the experts alike the first experts fill to exactly
+    C, which pins C; indices and counts are bit-exact with the oracle in
+    re-route and drop mode."""
+    if E == 8:
+        shape = TEST_SHAPES["mixtral_small"].with_(T=T, E=E, k=k)
+    else:
+        shape = TEST_SHAPES["v3_small"].with_(T=T, E=E, k=k)
+    shape = shape.with_(capacity_factor=cf, drop_tokens=drop)
+    C = math.ceil(cf * T * k / E)
+    assert C == math.ceil(Fraction(repr(cf)) * T * k / E)   # the decimal value
+    assert oracle.capacity(shape, T) == C
+    rng = np.random.default_rng(T + E + int(drop))
+    if ranking == "shared":
+        L = np.tile(np.linspace(1.0, -1.0, E, dtype=np.float32), (T, 1))
+        L += rng.standard_normal((T, E)).astype(np.float32) * 1e-3
+    else:
+        L = (rng.standard_normal((T, E)) + zipf_logit_offsets(E, 1.2, 3) * 2.0).astype(np.float32)
+    sb = rng.uniform(-0.05, 0.05, E).astype(np.float32) if shape.scoring == "sigmoid" else None
+    cfg = moe.make_config(shape)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    idx, w = moe.route(cfg, T, logits_in=torch.from_numpy(L).cuda(),
+                       sel_bias=None if sb is None else torch.from_numpy(sb).cuda(), expert_counts=counts)
+    torch.cuda.synchronize()
+    oidx, ow, _, oc = oracle.select(shape, L, sb)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
+    assert oc.max() <= C
+    if ranking == "shared":
+        assert oc.max() == C
+
+
 def test_all_tokens_to_one_expert():
     shape = TEST_SHAPES["mixtral_small"].with_(T=700)
     inp = make_inputs(shape, device="cuda")
@@ -569,14 +612,33 @@ def test_top1_single_group():
 
 
 def test_empty_batch_leaves_output_untouched():
+    """T == 0 is a successful no-op: every output buffer passed in (here
+    non-empty and pre-filled) keeps its contents, for the layer and the
+    router; the permutation reports zero rows for every expert."""
     shape = TEST_SHAPES["v3_small"]
     inp = make_inputs(shape, device="cuda", T=1)
     cfg = moe.make_config(shape, out_dtype="f32")
     x0 = inp["x"][:0]
-    out = torch.full((0, shape.H), 7.0, device="cuda")
-    moe.forward(cfg, x0, inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], sel_bias=inp["sel_bias"],
-                out=out)
+    E, k = shape.E, shape.k
+    out = torch.full((4, shape.H), 7.0, device="cuda")
+    idx = torch.full((4, k), 7, dtype=torch.int32, device="cuda")
+    w = torch.full((4, k), 7.0, dtype=torch.float32, device="cuda")
+    counts = torch.full((E,), 7, dtype=torch.int32, device="cuda")
+    logits = torch.full((4, E), 7.0, dtype=torch.float32, device="cuda")
+    L = moe.lib()
+    st = L.moe_forward(ctypes.byref(cfg), 0, moe._p(x0), moe._p(inp["w_router"]), None, moe._p(inp["sel_bias"]),
+                       moe._p(inp["w_gate"]), moe._p(inp["w_up"]), moe._p(inp["w_down"]), moe._p(out), moe._p(idx),
+                       moe._p(w), moe._p(counts), moe._p(logits), None, 0, moe._stream(None))
+    assert st == 0
+    st = L.moe_route(ctypes.byref(cfg), 0, moe._p(x0), moe._p(inp["w_router"]), None, moe._p(inp["sel_bias"]),
+                     None, moe._p(logits), moe._p(idx), moe._p(w), moe._p(counts), None, 0, moe._stream(None))
+    assert st == 0
     torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((idx == 7).all()) and bool((w == 7.0).all())
+    assert bool((counts == 7).all()) and bool((logits == 7.0).all())
+    c, off, _, _ = moe.permute(cfg, torch.empty((0, k), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert bool((c == 0).all()) and bool((off == 0).all())
 
 
 def test_deterministic_bitwise():

@@ -3,7 +3,7 @@
 Source: "15. DeepSeek：MLA、MoE 与 MTP", section "V3 的 MoE：256 个专家怎样选 8
 个" (per step, an overloaded expert's bias is lowered by gamma and an idle one's
 raised; gamma = 0.001; monitor each expert's token share and the bias drift);
-"GPT-4 Has 1.8 Trillion Parameters. It Uses 2% of Them Per Token", section 4.4
+"GPT-4稀疏激活原理：2%参数调用背后的MoE工程实践", section 4.4
 (the entropy of the expert calls as a health signal).
 """
 import math

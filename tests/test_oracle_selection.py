@@ -282,6 +282,33 @@ def test_capacity_matches_sequential_simulation(E, G, keep, k, cf, scoring):
             np.testing.assert_allclose(w[t, :n].sum(), tot, rtol=1e-13)
 
 
+@pytest.mark.parametrize("cf", ["1.0", "1.2", "1.25", "0.3", "2.0"])
+def test_capacity_value_is_the_decimal_ceiling_for_the_pages_factors(cf):
+    """C = ceil(cf * T * k / E) with cf the decimal the configuration states
+    (capacity_factor: 1.2 in the GPT-4 page's config block, 1.25 at the
+    decode workload), checked with exact rational arithmetic over every T up
+    to 3000 at the workloads' (k, E).  The oracle (and the library) evaluate
+    ((cf*T)*k)/E in IEEE double on the double nearest the decimal; for these
+    factors that never crosses an integer the exact value does not."""
+    q = Fraction(cf)
+    for k, E in ((2, 8), (6, 160), (8, 256)):
+        for T in range(1, 3001):
+            want = math.ceil(q * T * k / E)
+            assert oracle.capacity(shape(T=T, E=E, k=k, capacity_factor=float(cf)), T) == want, (cf, T, k, E)
+
+
+def test_capacity_of_a_factor_stored_above_its_decimal():
+    """The reading's one visible edge: 1.1 is stored as a double slightly
+    above 1.1, so where 1.1 * T * k / E is an integer in decimal the IEEE
+    double evaluation lands just above it and C is one more (T = 200, k = 2,
+    E = 8: decimal 55, double 56).  Both sides of the build use the double
+    value, so they agree with each other."""
+    assert math.ceil(Fraction("1.1") * 200 * 2 / 8) == 55
+    assert Fraction(1.1) > Fraction("1.1")
+    assert oracle.capacity(shape(T=200, E=8, k=2, capacity_factor=1.1), 200) == 56
+    assert oracle.capacity(shape(T=320, E=256, k=8, capacity_factor=1.1), 320) == 11
+
+
 def test_capacity_defining_property_v3_decode_shape():
     """At the decode workload's routing shape: every expert that ranks above a
     chosen one (or above an empty slot) but was not chosen was full when the
