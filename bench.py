@@ -11,7 +11,14 @@ down GEMM, combine.  Default workload: the DeepSeek-V3-shaped prefill layer
 Prints one JSON line: tokens/s of the whole job, the roofline of the dominant
 kernel (gate/up + SwiGLU grouped GEMM on the bf16 or fp8 matrix cores) timed
 live with HIP events on the launch stream, and the CPU oracle timed on a
-bounded token sample.
+bounded token sample.  The same line carries
+ - "decode": the decode-sized layer of the same model (128 tokens, capacity
+   factor 1.25, Zipf-skewed load), which is bound by reading the weights of
+   the experts it touches: ms per layer, touched experts, weight bytes and the
+   fraction of HBM bandwidth, per kernel;
+ - "attainable": the sustained bf16 matrix-core rate and the HBM streaming
+   read rate of this GPU, measured with the library's own probe kernels, and
+   the layer's rates as fractions of them next to the nominal peaks.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
 """
@@ -59,6 +66,16 @@ def measured_traffic(workload, dtype):
     return float(val.group(1))
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(shape, inp, target_s):
     """The fp64 oracle on a bounded sample of the same workload's tokens."""
     import numpy as np
@@ -103,42 +120,20 @@ def cpu_baseline(shape, inp, target_s):
     n = n1 + n2
     secs = t1 + t2
     log("cpu baseline: %d tokens in %.1f s on %d threads" % (n, secs, cores))
-    return {"value": n / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": n / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d random tokens of the %d-token %s batch: router logits, selection, %d routed + %d shared "
                       "SwiGLU experts each and the combine, fp64, %.1f s" % (n, shape.T, shape.name, shape.k,
                                                                           shape.S, secs)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="deepseek_v3_prefill")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--capacity-factor", type=float, default=None,
-                    help="override the workload's capacity factor (<= 0: unlimited)")
-    ap.add_argument("--drop-tokens", action="store_true", help="with a capacity: drop the overflow")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="copy 1 GiB device-to-device 3 times first (reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(shape, steps, warmup, dev):
+    """Time `steps` layer calls (after `warmup`) of one workload; per-kernel
+    launch times from the library's HIP events on the launch stream."""
     import torch
 
     import routing_expert_ffn_amd as moe
-    from workloads import CONFIGS, make_inputs
+    from workloads import make_inputs
 
-    shape = CONFIGS[args.workload]
-    if args.capacity_factor is not None or args.drop_tokens:
-        cf = shape.capacity_factor if args.capacity_factor is None else args.capacity_factor
-        shape = shape.with_(capacity_factor=cf, drop_tokens=args.drop_tokens)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     log("generating inputs for", shape.name)
     inp = make_inputs(shape, device=dev)
     cfg = moe.make_config(shape, out_dtype="bf16")
@@ -147,15 +142,6 @@ def main():
     out = torch.empty((T, shape.H), dtype=torch.bfloat16, device=dev)
     idx = torch.empty((T, shape.k), dtype=torch.int32, device=dev)
     counts = torch.empty((shape.E,), dtype=torch.int32, device=dev)
-
-    if args.calibrate_copy:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log("calibration: 3 device copies of 1 GiB")
 
     def step():
         if shape.dtype == "fp8":
@@ -171,39 +157,157 @@ def main():
                         logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], out=out, topk_idx=idx,
                         expert_counts=counts, ws=ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log("warmup done")
+    log("%s: warmup done" % shape.name)
 
-    moe.timing_enable(args.steps * 16)
+    moe.timing_enable(steps * 16)
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     kern = moe.timing_read()
     moe.timing_enable(0)
-    log("timed %d steps: %.3f ms/step" % (args.steps, total_ms / args.steps))
+    log("%s: timed %d steps: %.3f ms/step" % (shape.name, steps, total_ms / steps))
 
     assigned = int((idx >= 0).sum().item())
-    rows = assigned + shape.S * T
-    gateup_flops = 4.0 * shape.H * shape.I * rows
-    down_flops = 2.0 * shape.H * shape.I * rows
-    layer_flops = shape.flops(assigned)
-    ms_step = total_ms / args.steps
-    kernels = {name: ms / n for name, (ms, n) in kern.items()}
-    gu_ms = kernels.get("gateup_swiglu")
-    achieved = gateup_flops / (gu_ms * 1e-3) / 1e12
     touched = int((counts > 0).sum().item())
     wsz = {"fp8": 1, "bf16": 2, "f32": 4}[shape.dtype]
-    weight_bytes = (touched + shape.S) * 3 * shape.H * shape.I * wsz
+    per_expert = 3 * shape.H * shape.I * wsz
     if shape.dtype == "fp8":  # plus the UE8M0 block scales
-        weight_bytes += (touched + shape.S) * 3 * (shape.H // 128) * (shape.I // 128)
+        per_expert += 3 * (shape.H // 128) * (shape.I // 128)
+    return {"inp": inp, "ms_step": total_ms / steps, "kernels": {name: ms / n for name, (ms, n) in kern.items()},
+            "assigned": assigned, "touched": touched, "weight_bytes": (touched + shape.S) * per_expert,
+            "gateup_weight_bytes": (touched + shape.S) * per_expert * 2 // 3,
+            "down_weight_bytes": (touched + shape.S) * per_expert // 3}
+
+
+def decode_record(shape, r):
+    """The decode-sized layer: weight-read bound."""
+    ms = r["ms_step"]
+    k = r["kernels"]
+    gbs = r["weight_bytes"] / (ms * 1e-3) / 1e9
+    rec = {"workload": shape.name, "tokens": shape.T, "capacity_factor": shape.capacity_factor,
+           "ms_per_layer": ms, "tokens_per_s": shape.T / (ms * 1e-3), "touched_experts": r["touched"],
+           "assigned_slots": r["assigned"], "weight_bytes": r["weight_bytes"], "weight_gbs": gbs,
+           "hbm_frac": gbs / PEAK_HBM_GBS, "kernels_ms": k}
+    for name, key in (("gateup_swiglu", "gateup_weight_bytes"), ("down", "down_weight_bytes")):
+        if k.get(name):
+            rec[name + "_weight_gbs"] = r[key] / (k[name] * 1e-3) / 1e9
+    # HBM bytes of one gate/up launch from the committed counter summary (null
+    # when it was taken on another kernel source)
+    rec["gateup_traffic"] = measured_traffic(shape.name, shape.dtype)
+    return rec
+
+
+def attainable_rates(dev, mfma_seconds=1.2):
+    """Sustained bf16 MFMA rate (about mfma_seconds of back-to-back launches;
+    operands that change between instructions, as in a GEMM, and for
+    comparison one fixed operand pair) and HBM streaming read rate of this
+    GPU, from the library's probe kernels."""
+    import torch
+
+    import routing_expert_ffn_amd as moe
+
+    stream = torch.cuda.current_stream()
+    blocks = 1024
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()                                     # warm-up launch
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    out = {}
+    for vary, key in ((True, "mfma_bf16_tflops"), (False, "mfma_bf16_tflops_fixed_operands")):
+        # size one launch to about a quarter of the target, then time four
+        iters = 20000
+        ms = timed(lambda: moe.probe_mfma_bf16(blocks, iters, sink, vary=vary), 1)
+        iters = max(1, int(iters * (mfma_seconds * 250.0) / ms))
+        flops = moe.probe_mfma_bf16(blocks, iters, sink, vary=vary)
+        ms = timed(lambda: moe.probe_mfma_bf16(blocks, iters, sink, vary=vary), 4)
+        out[key] = flops / (ms * 1e-3) / 1e12
+        log("probe: bf16 MFMA %.0f TFLOP/s sustained, %s operands (4 launches of %.0f ms)"
+            % (out[key], "varying" if vary else "fixed", ms))
+    out["mfma_seconds"] = 5 * ms * 1e-3
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    read = {}
+    rblocks = 256 * 8
+    rsink = torch.empty(rblocks * 256, dtype=torch.float32, device=dev)
+    for mode, name in ((0, "plain"), (1, "nontemporal"), (2, "to_lds"), (3, "to_lds_nontemporal")):
+        rms = timed(lambda: moe.probe_read(buf, mode, rblocks, rsink), 10)
+        read[name] = nbytes / (rms * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    log("probe: HBM read %s GB/s" % ", ".join("%s %.0f" % kv for kv in read.items()))
+    out.update({"hbm_read_gbs": max(read.values()), "hbm_read_gbs_by_mode": read, "hbm_read_bytes": nbytes})
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="deepseek_v3_prefill")
+    ap.add_argument("--decode-workload", default="deepseek_v3_decode",
+                    help="decode-sized workload measured after the main one ('' to skip)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-rate probes")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--capacity-factor", type=float, default=None,
+                    help="override the workload's capacity factor (<= 0: unlimited)")
+    ap.add_argument("--drop-tokens", action="store_true", help="with a capacity: drop the overflow")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="copy 1 GiB device-to-device 3 times first (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from workloads import CONFIGS
+
+    shape = CONFIGS[args.workload]
+    if args.capacity_factor is not None or args.drop_tokens:
+        cf = shape.capacity_factor if args.capacity_factor is None else args.capacity_factor
+        shape = shape.with_(capacity_factor=cf, drop_tokens=args.drop_tokens)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration: 3 device copies of 1 GiB")
+
+    r = run_workload(shape, args.steps, args.warmup, dev)
+    T = shape.T
+    rows = r["assigned"] + shape.S * T
+    gateup_flops = 4.0 * shape.H * shape.I * rows
+    layer_flops = shape.flops(r["assigned"])
+    ms_step = r["ms_step"]
+    kernels = r["kernels"]
+    gu_ms = kernels.get("gateup_swiglu")
+    achieved = gateup_flops / (gu_ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if shape.dtype == "fp8" else PEAK_BF16_TFLOPS
     res = {
         "metric": METRIC,
@@ -228,11 +332,11 @@ def main():
                      "kernel": "gateup_swiglu", "flops_per_launch": gateup_flops, "ms_per_launch": gu_ms},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
         "layer_mfma_frac": layer_flops / (ms_step * 1e-3) / 1e12 / peak,
-        "layer_weight_gbs": weight_bytes / (ms_step * 1e-3) / 1e9,
-        "layer_hbm_frac": weight_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "layer_weight_gbs": r["weight_bytes"] / (ms_step * 1e-3) / 1e9,
+        "layer_hbm_frac": r["weight_bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels_ms": kernels,
-        "assigned_slots": assigned,
-        "touched_experts": touched,
+        "assigned_slots": r["assigned"],
+        "touched_experts": r["touched"],
     }
     if shape.T <= 1024:
         # decode-sized: the weight stream is the bound
@@ -240,9 +344,27 @@ def main():
                            "unit": "GB/s", "frac": res["layer_hbm_frac"], "traffic": None,
                            "kernel": "whole layer (weights of touched experts)"}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(shape, r["inp"], args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
+    del r
+    torch.cuda.empty_cache()
+
+    if args.decode_workload and args.decode_workload != shape.name:
+        dshape = CONFIGS[args.decode_workload]
+        d = run_workload(dshape, args.steps, args.warmup, dev)
+        res["decode"] = decode_record(dshape, d)
+        del d
+        torch.cuda.empty_cache()
+
+    if not args.no_peaks:
+        att = attainable_rates(dev)
+        if shape.dtype == "bf16":
+            att["layer_frac_of_attainable_mfma"] = res["layer_tflops"] / att["mfma_bf16_tflops"]
+            att["gateup_frac_of_attainable_mfma"] = achieved / att["mfma_bf16_tflops"]
+        if "decode" in res:
+            att["decode_frac_of_attainable_hbm"] = res["decode"]["weight_gbs"] / att["hbm_read_gbs"]
+        res["attainable"] = att
     print(json.dumps(res), flush=True)
 
 

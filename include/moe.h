@@ -285,6 +285,28 @@ moe_status moe_quantize_fp8(int64_t rows, int32_t K, const void* in, uint8_t* co
 moe_status moe_balance_update(const moe_config* cfg, const int32_t* expert_counts, float* sel_bias, float gamma,
                               float* share, float* stats, void* stream);
 
+/* Attainable-rate probes: the library's own kernels measuring what the part
+ * delivers, so that the layer's rates can be quoted against the sustained
+ * rates of the same chip at its power limit as well as against the nominal
+ * peaks.  Each enqueues one kernel on `stream` (timed by the caller) and
+ * writes blocks * 256 floats to the device array `sink` (values without
+ * meaning, written so nothing is optimised away).
+ * moe_probe_mfma_bf16: `blocks` workgroups of four wavefronts, each wavefront
+ *   issuing `iters` rounds of eight independent v_mfma_f32_32x32x16_bf16 on
+ *   pseudo-random register operands: vary = 1 takes four A and four B
+ *   fragments in turn (inputs change between instructions, as in a GEMM),
+ *   vary = 0 one fixed pair; *flops (host) gets the FLOPs the launch
+ *   performs (blocks * iters * 4 * 8 * 32768).
+ * moe_probe_read: reads the `bytes` (a positive multiple of 16) of the
+ *   16-byte aligned device buffer `buf` once, in 16-byte pieces with eight in
+ *   flight per lane, over `blocks` workgroups of 256 threads; mode 0: plain
+ *   loads, 1: non-temporal loads, 2: global->LDS copies (the form the expert
+ *   GEMMs stream their operands in), 3: global->LDS copies with the
+ *   non-temporal policy. */
+moe_status moe_probe_mfma_bf16(int32_t vary, int32_t blocks, int64_t iters, float* sink, double* flops,
+                               void* stream);
+moe_status moe_probe_read(int32_t mode, int32_t blocks, const void* buf, size_t bytes, float* sink, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* moe_last_error(void);
 

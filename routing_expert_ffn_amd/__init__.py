@@ -21,9 +21,9 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
           -4: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8", "moe_quantize_fp8",
-           "moe_balance_update", "moe_last_error", "moe_version", "moe_timing_enable", "moe_timing_read",
-           "moe_kernel_name")
+           "moe_forward", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8",
+           "moe_quantize_fp8", "moe_balance_update", "moe_probe_mfma_bf16", "moe_probe_read", "moe_last_error",
+           "moe_version", "moe_timing_enable", "moe_timing_read", "moe_kernel_name")
 
 
 class MoeError(RuntimeError):
@@ -71,8 +71,9 @@ def lib():
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         C = ctypes.POINTER(moe_config)
         for name in ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn",
-                     "moe_combine", "moe_forward", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8",
-                     "moe_quantize_fp8", "moe_balance_update", "moe_timing_enable", "moe_timing_read"):
+                     "moe_combine", "moe_forward", "moe_forward_hash", "moe_forward_fp8",
+                     "moe_expert_ffn_fp8", "moe_quantize_fp8", "moe_balance_update", "moe_timing_enable",
+                     "moe_timing_read", "moe_probe_mfma_bf16", "moe_probe_read"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [C, I64, ctypes.POINTER(SZ)]
         L.moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -86,6 +87,8 @@ def lib():
         L.moe_forward_fp8.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_expert_ffn_fp8.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_quantize_fp8.argtypes = [I64, I32, P, P, P, I32, P]
+        L.moe_probe_mfma_bf16.argtypes = [I32, I32, I64, P, ctypes.POINTER(ctypes.c_double), P]
+        L.moe_probe_read.argtypes = [I32, I32, P, SZ, P, P]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_version.restype = ctypes.c_char_p
@@ -288,6 +291,28 @@ def quantize_fp8(x, scale_stride=None, stream=None):
     scales = torch.zeros((rows, ss), dtype=torch.uint8, device=x.device)
     _check(lib().moe_quantize_fp8(rows, K, _p(x), _p(codes), _p(scales), ss, _stream(stream)))
     return codes, scales
+
+
+def probe_mfma_bf16(blocks, iters, sink, vary=True, stream=None):
+    """Enqueue the sustained bf16 matrix-core probe (vary: four A and four B
+    fragments in turn, else one fixed pair); `sink` is a float32 device
+    tensor of at least blocks * 256 elements.  -> FLOPs of the launch."""
+    assert sink.dtype == torch.float32 and sink.numel() >= blocks * 256
+    f = ctypes.c_double(0.0)
+    _check(lib().moe_probe_mfma_bf16(1 if vary else 0, int(blocks), int(iters), _p(sink), ctypes.byref(f),
+                                     _stream(stream)))
+    return f.value
+
+
+def probe_read(buf, mode, blocks, sink, stream=None):
+    """Enqueue the streaming read probe over the device tensor `buf` (mode 0
+    plain loads, 1 non-temporal loads, 2 global->LDS copies, 3 the same
+    non-temporal); `sink` is a float32 device tensor of at least blocks * 256
+    elements.  -> bytes read."""
+    assert sink.dtype == torch.float32 and sink.numel() >= blocks * 256
+    n = buf.numel() * buf.element_size()
+    _check(lib().moe_probe_read(int(mode), int(blocks), _p(buf), n, _p(sink), _stream(stream)))
+    return n
 
 
 def timing_enable(max_launches):

@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["router.hip", "permute.hip", "gemm.hip", "gemm_fp8.hip", "combine.hip", "balance.hip", "api.cpp"]
+SOURCES = ["router.hip", "permute.hip", "gemm.hip", "gemm_fp8.hip", "combine.hip", "balance.hip", "probe.hip",
+           "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -242,6 +242,13 @@ hipError_t run_router(const Dims& d, RouterArgs a, const void* x, const void* w_
                       hipStream_t s) {
   if (a.logits_in) return timed(K_ROUTE_SELECT, s, [&] { return launch_route_select(a, s); });
   if (d.xdt != MOE_BF16) return timed(K_ROUTER, s, [&] { return launch_router(a, d.xdt, s); });
+  if (router_fused_applies(d.T, d.E)) {
+    // GEMM and selection in one kernel; the logits are written only when the
+    // caller (or the capacity pass) asked for them
+    a.x = x;
+    a.w_router = w_router;
+    return timed(K_ROUTER, s, [&] { return launch_router_fused(a, s); });
+  }
   int sps;
   const int S = router_splits(d.T, d.H, d.E, &sps);
   float* lg = a.logits_out ? a.logits_out : at<float>(ws, L.logits);
@@ -828,6 +835,28 @@ moe_status moe_balance_update(const moe_config* cfg, const int32_t* expert_count
   const hipError_t e = timed(K_BALANCE, s, [&] { return launch_balance(a, s); });
   if (e != hipSuccess) return hip_fail(e, "balance kernel launch");
   return MOE_OK;
+}
+
+moe_status moe_probe_mfma_bf16(int32_t vary, int32_t blocks, int64_t iters, float* sink, double* flops,
+                               void* stream) {
+  if (vary != 0 && vary != 1) return fail(MOE_ERR_INVALID_ARG, "vary must be 0 or 1");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "blocks must be in [1, 2^20]");
+  if (iters < 1) return fail(MOE_ERR_INVALID_ARG, "iters must be >= 1");
+  if (!sink || !flops) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  *flops = (double)blocks * (double)iters * probe_mfma_flops_per_iter_block();
+  const hipError_t e = launch_probe_mfma(vary, blocks, iters, sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "MFMA probe launch");
+}
+
+moe_status moe_probe_read(int32_t mode, int32_t blocks, const void* buf, size_t bytes, float* sink, void* stream) {
+  if (mode < 0 || mode > 3) return fail(MOE_ERR_INVALID_ARG, "mode must be 0, 1, 2 or 3");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "blocks must be in [1, 2^20]");
+  if (!buf || !sink) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (!aligned16(buf) || bytes % 16 != 0 || bytes == 0)
+    return fail(MOE_ERR_INVALID_ARG, "buf must be 16-byte aligned and bytes a positive multiple of 16");
+  const hipError_t e =
+      launch_probe_read(mode, blocks, buf, (int64_t)(bytes / 16), sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "read probe launch");
 }
 
 const char* moe_last_error(void) { return g_err.c_str(); }

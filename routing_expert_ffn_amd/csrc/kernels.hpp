@@ -203,6 +203,10 @@ hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s);
 // its launch.
 int router_splits(int64_t T, int H, int E, int* sps);
 hipError_t launch_router_gemm(const RouterGemmArgs& a, hipStream_t s);
+// Fused bf16 router GEMM + selection for large batches (a.x, a.w_router;
+// logits written to a.logits_out only when it is set).
+bool router_fused_applies(int64_t T, int E);
+hipError_t launch_router_fused(const RouterArgs& a, hipStream_t s);
 // Selection from partial logits (a.part, a.nsplit) or from a.logits_in.
 hipError_t launch_route_select(const RouterArgs& a, hipStream_t s);
 hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s);
@@ -227,3 +231,12 @@ hipError_t launch_row_scales(const RowScaleArgs& a, hipStream_t s);
 hipError_t launch_pack_scales(const ScalePackArgs& a, hipStream_t s);
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStream_t s);
+// Attainable-rate probes (probe.hip): threads per block, FLOPs of one loop
+// iteration of one block of the MFMA probe, and the launches.
+int probe_threads();
+double probe_mfma_flops_per_iter_block();
+// vary: four A and four B fragments in turn (1) or one fixed pair (0)
+hipError_t launch_probe_mfma(int vary, int blocks, int64_t iters, float* sink, hipStream_t s);
+// mode 0: plain loads, 1: non-temporal loads, 2: global->LDS copies, 3: the
+// same with the non-temporal policy
+hipError_t launch_probe_read(int mode, int blocks, const void* buf, int64_t n16, float* sink, hipStream_t s);

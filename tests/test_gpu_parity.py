@@ -336,13 +336,17 @@ def test_layer_many_experts_and_slots(E, G, tg, k):
 
 
 @pytest.mark.parametrize("T,H,E", [(8200, 7168, 256), (12811, 1024, 96), (16461, 1024, 200), (8200, 256, 64),
-                                   (8063, 2048, 256)])
+                                   (8063, 2048, 256), (16384, 7168, 256), (16320, 1024, 256), (16321, 512, 128),
+                                   (20000, 4096, 256)])
 def test_router_gemm_large_batches(T, H, E):
     """The router GEMM at large batch sizes (128-token tiles at one workgroup
     per compute unit, K split into slices, ragged last token tile, ragged last
-    slice, slices of one step) and just below them (64-token tiles): logits of every token
-    of the first and last tiles and of a sample in between against the
-    oracle's dot products, and the routing of the GPU logits bit-exact."""
+    slice, slices of one step), just below them (64-token tiles), and from 256
+    tiles of 64 tokens on (16321 tokens and more: the fused kernel, GEMM over
+    the whole K and selection in one launch, 128 or 256 expert columns, ragged
+    last tile): logits of every token of the first and last tiles and of a
+    sample in between against the oracle's dot products, and the routing of
+    the GPU logits bit-exact."""
     shape = TEST_SHAPES["v3_small"].with_(T=T, H=H, E=E, G=8 if E % 8 == 0 else 1,
                                          topk_group=4 if E % 8 == 0 else 1)
     g = torch.Generator(device="cuda")
@@ -364,6 +368,36 @@ def test_router_gemm_large_batches(T, H, E):
     assert np.array_equal(idx.cpu().numpy(), oidx)
     assert np.array_equal(counts.cpu().numpy(), oc)
     np.testing.assert_allclose(wts.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("cf", [0.0, 1.25])
+def test_fused_router_without_logits_output(cf):
+    """The fused large-batch router writes the logits only when asked: the
+    selection is the same with and without a logits output, and (unlimited
+    routing) bit-exact with the oracle run on the GPU's logits; with a
+    capacity limit the logits go to the workspace for the capacity pass."""
+    T, H, E = 16400, 1024, 256
+    shape = TEST_SHAPES["v3_small"].with_(T=T, H=H, E=E, capacity_factor=cf)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((E, H), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
+    sb = (torch.rand((E,), generator=g, device="cuda") * 0.1 - 0.05).contiguous()
+    lb = torch.from_numpy(zipf_logit_offsets(E, 1.1, 5)).cuda() if cf > 0 else None
+    cfg = moe.make_config(shape)
+    lo = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    c1 = torch.empty(E, dtype=torch.int32, device="cuda")
+    c2 = torch.empty(E, dtype=torch.int32, device="cuda")
+    i1, w1 = moe.route(cfg, T, x=x, w_router=w, logit_bias=lb, sel_bias=sb, logits_out=lo, expert_counts=c1)
+    i2, w2 = moe.route(cfg, T, x=x, w_router=w, logit_bias=lb, sel_bias=sb, expert_counts=c2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(w1, w2) and torch.equal(c1, c2)
+    oidx, ow, _, oc = oracle.select(shape, lo.cpu().numpy(), sb.cpu().numpy())
+    assert np.array_equal(i1.cpu().numpy(), oidx)
+    assert np.array_equal(c1.cpu().numpy(), oc)
+    np.testing.assert_allclose(w1.cpu().numpy(), ow, rtol=1e-5, atol=1e-6)
+    if cf > 0:
+        assert oc.max() == oracle.capacity(shape, T)
 
 
 # ---- routing edge cases ------------------------------------------------------------
