@@ -222,6 +222,24 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
                        const void* w_down, void* out, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
                        float* logits_out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Every argument but ws and ws_bytes as moe_forward;
+ * the caller still passes every input and output.  The workspace is a static
+ * device array of the library, 64 MiB per GPU, held until the process ends
+ * (enough for the DeepSeek-V3-shaped layer up to about 200 tokens): a layer
+ * and batch whose moe_workspace_size exceeds 64 MiB are rejected with
+ * MOE_ERR_WORKSPACE before anything is enqueued.  No device memory is
+ * allocated or freed.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (nothing in it is assumed zero): calls that
+ * may overlap on one GPU (two host threads, or two streams without an order
+ * between them) race and must be serialised by the caller.  Not for MOE_FP8
+ * layers (MOE_ERR_INVALID_ARG). */
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                               const float* logit_bias, const float* sel_bias, const void* w_gate, const void* w_up,
+                               const void* w_down, void* out, int32_t* topk_idx, float* topk_w,
+                               int32_t* expert_counts, float* logits_out, void* stream);
+
 /* moe_forward with hash routing (moe_route_hash's selection): token_ids,
  * tid2eid and vocab as there, every other argument as moe_forward. */
 moe_status moe_forward_hash(const moe_config* cfg, int64_t T, const void* x, const void* w_router,

@@ -21,7 +21,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
           -4: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8",
+           "moe_forward", "moe_forward_noalloc", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8",
            "moe_quantize_fp8", "moe_balance_update", "moe_probe_mfma_bf16", "moe_probe_read", "moe_last_error",
            "moe_version", "moe_timing_enable", "moe_timing_read", "moe_kernel_name")
 
@@ -71,7 +71,7 @@ def lib():
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         C = ctypes.POINTER(moe_config)
         for name in ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn",
-                     "moe_combine", "moe_forward", "moe_forward_hash", "moe_forward_fp8",
+                     "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_forward_hash", "moe_forward_fp8",
                      "moe_expert_ffn_fp8", "moe_quantize_fp8", "moe_balance_update", "moe_timing_enable",
                      "moe_timing_read", "moe_probe_mfma_bf16", "moe_probe_read"):
             getattr(L, name).restype = ctypes.c_int
@@ -82,6 +82,7 @@ def lib():
         L.moe_combine.argtypes = [C, I64, P, P, P, P, P]
         L.moe_balance_update.argtypes = [C, P, P, ctypes.c_float, P, P, P]
         L.moe_forward.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_forward_noalloc.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.moe_route_hash.argtypes = [C, I64, P, P, P, P, P, P, P, I64, P, P, P, P, SZ, P]
         L.moe_forward_hash.argtypes = [C, I64, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_forward_fp8.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -231,6 +232,17 @@ def forward(cfg, x, w_router, w_gate, w_up, w_down, logit_bias=None, sel_bias=No
     _check(lib().moe_forward(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(sel_bias), _p(w_gate),
                              _p(w_up), _p(w_down), _p(out), _p(topk_idx), _p(topk_w), _p(expert_counts),
                              _p(logits_out), _p(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def forward_noalloc(cfg, x, w_router, w_gate, w_up, w_down, out, logit_bias=None, sel_bias=None, topk_idx=None,
+                    topk_w=None, expert_counts=None, logits_out=None, stream=None):
+    """The whole layer on the library's static device scratch (no workspace
+    argument); `out` [T,H] in cfg.out_dtype is required.  -> out"""
+    T = x.shape[0]
+    _check(lib().moe_forward_noalloc(ctypes.byref(cfg), T, _p(x), _p(w_router), _p(logit_bias), _p(sel_bias),
+                                     _p(w_gate), _p(w_up), _p(w_down), _p(out), _p(topk_idx), _p(topk_w),
+                                     _p(expert_counts), _p(logits_out), _stream(stream)))
     return out
 
 

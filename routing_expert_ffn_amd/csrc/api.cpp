@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -45,6 +46,36 @@ hipError_t timed(int id, hipStream_t s, F&& f) {
     return err;
   }
   return f();
+}
+
+// ---- static scratch of moe_forward_noalloc ---------------------------------------
+// The workspace of moe_forward_noalloc: a device array of the code object,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address of the current GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 // ---- configuration -------------------------------------------------------------
@@ -763,6 +794,27 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
   if (st != MOE_OK) return st;
   return forward_impl(d, x, w_router, logit_bias, sel_bias, w_gate, w_up, w_down, out, topk_idx, topk_w,
                       expert_counts, logits_out, ws, ws_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                               const float* logit_bias, const float* sel_bias, const void* w_gate, const void* w_up,
+                               const void* w_down, void* out, int32_t* topk_idx, float* topk_w,
+                               int32_t* expert_counts, float* logits_out, void* stream) {
+  Dims d;
+  const moe_status st = check_config(cfg, T, d);
+  if (st != MOE_OK) return st;
+  if (d.fp8) return fail(MOE_ERR_INVALID_ARG, "MOE_FP8 layers run through moe_forward_fp8");
+  const size_t need = layout_of(d).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "this layer and batch need " + std::to_string(need) +
+                                       " bytes of workspace; the static scratch holds " +
+                                       std::to_string(kScratchBytes) + ": call moe_forward with a workspace");
+  if (T == 0) return MOE_OK;
+  void* ws = nullptr;
+  const moe_status sst = scratch_of_current_device(&ws);
+  if (sst != MOE_OK) return sst;
+  return forward_impl(d, x, w_router, logit_bias, sel_bias, w_gate, w_up, w_down, out, topk_idx, topk_w,
+                      expert_counts, logits_out, ws, kScratchBytes, static_cast<hipStream_t>(stream), nullptr);
 }
 
 moe_status moe_forward_fp8(const moe_config* cfg, int64_t T, const void* x, const void* w_router,

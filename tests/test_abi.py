@@ -55,6 +55,22 @@ def test_config_struct_layout_matches_the_header(tmp_path):
     assert moe.moe_config.capacity_factor.size == 8
 
 
+def test_noalloc_checks_its_scratch_limit_before_any_launch():
+    """moe_forward_noalloc runs on a 64 MiB static scratch: a layer and batch
+    whose workspace is larger is rejected with MOE_ERR_WORKSPACE (and FP8
+    layers with MOE_ERR_INVALID_ARG) before any HIP call; T == 0 is a no-op."""
+    L = moe.lib()
+    nulls = [None] * 12
+    cfg = moe.make_config(CONFIGS["deepseek_v3_prefill"])
+    assert moe.workspace_size(cfg, 16384) > 64 << 20
+    assert L.moe_forward_noalloc(ctypes.byref(cfg), 16384, *nulls, None) == -3
+    assert "static scratch" in L.moe_last_error().decode()
+    assert moe.workspace_size(cfg, 128) <= 64 << 20
+    assert L.moe_forward_noalloc(ctypes.byref(cfg), 0, *nulls, None) == 0
+    cfg8 = moe.make_config(CONFIGS["deepseek_v3_decode_fp8"])
+    assert L.moe_forward_noalloc(ctypes.byref(cfg8), 128, *nulls, None) == -1
+
+
 def test_version_and_clean_error_state():
     assert "gfx950" in moe.version()
 
