@@ -273,13 +273,6 @@ hipError_t run_router(const Dims& d, RouterArgs a, const void* x, const void* w_
                       hipStream_t s) {
   if (a.logits_in) return timed(K_ROUTE_SELECT, s, [&] { return launch_route_select(a, s); });
   if (d.xdt != MOE_BF16) return timed(K_ROUTER, s, [&] { return launch_router(a, d.xdt, s); });
-  if (router_fused_applies(d.T, d.E)) {
-    // GEMM and selection in one kernel; the logits are written only when the
-    // caller (or the capacity pass) asked for them
-    a.x = x;
-    a.w_router = w_router;
-    return timed(K_ROUTER, s, [&] { return launch_router_fused(a, s); });
-  }
   int sps;
   const int S = router_splits(d.T, d.H, d.E, &sps);
   float* lg = a.logits_out ? a.logits_out : at<float>(ws, L.logits);

@@ -203,10 +203,6 @@ hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s);
 // its launch.
 int router_splits(int64_t T, int H, int E, int* sps);
 hipError_t launch_router_gemm(const RouterGemmArgs& a, hipStream_t s);
-// Fused bf16 router GEMM + selection for large batches (a.x, a.w_router;
-// logits written to a.logits_out only when it is set).
-bool router_fused_applies(int64_t T, int E);
-hipError_t launch_router_fused(const RouterArgs& a, hipStream_t s);
 // Selection from partial logits (a.part, a.nsplit) or from a.logits_in.
 hipError_t launch_route_select(const RouterArgs& a, hipStream_t s);
 hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s);

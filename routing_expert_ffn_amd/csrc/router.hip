@@ -595,162 +595,6 @@ __global__ __launch_bounds__(256) void router_gemm_big_kernel(RouterGemmArgs a) 
   }
 }
 
-// Fused router for large batches (at least 256 tiles of 64 tokens, at most
-// 256 experts): the GEMM over the whole K and the selection in one kernel, so
-// neither partial nor complete logits go through memory (they are written
-// only when the caller asks for them, or the capacity pass needs them).  One
-// workgroup per compute unit computes 64 tokens x 128*NB experts (wave w:
-// experts w*32*NB .., all 64 tokens, 2 x NB MFMA blocks).  x, read once from
-// HBM with the non-temporal policy, streams through an eight-stage LDS ring
-// copied seven steps ahead (56 KB in flight per compute unit: the rate of the
-// stream is the bytes in flight over the memory latency); the router weights,
-// re-read from L2 by every workgroup, through three stages copied two steps
-// ahead.  After the last step the logits tile (bias added) replaces the
-// stages in LDS and every wavefront routes 16 of the tile's tokens with the
-// selection code of route_select_kernel.
-constexpr int kRfTokens = 64, kRfAStages = 8, kRfBStages = 3;
-
-template <int NB>
-__global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
-  constexpr int NJ = 2 * NB;
-  constexpr int EP = 128 * NB;
-  constexpr int A_STAGE = kRfTokens * 128, B_STAGE = EP * 128;
-  constexpr int A_PER_WAVE = kRfTokens / 8 / 4, B_PER_WAVE = EP / 8 / 4;
-  constexpr int LA = kRfAStages - 1, LB = kRfBStages - 1;  // copy leads (steps)
-  constexpr int LROW = EP + 8;                               // logits row stride (floats)
-  constexpr int RING = kRfAStages * A_STAGE + kRfBStages * B_STAGE;
-  constexpr int TILE = kRfTokens * LROW * 4;
-  __shared__ __attribute__((aligned(1024))) char lds[RING > TILE ? RING : TILE];
-  const RouteParams& p = a.p;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kRfTokens;
-  const int nk = p.H / 64;
-  const int lrow = lane >> 3;
-  const bf16* x = static_cast<const bf16*>(a.x);
-  const bf16* w = static_cast<const bf16*>(a.w_router);
-  uint32_t aoff[A_PER_WAVE], boff[B_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < A_PER_WAVE; ++i) {
-    const int r = (wave * A_PER_WAVE + i) * 8 + lrow;
-    const int tok = min(t0 + r, p.T - 1);
-    aoff[i] = (uint32_t)tok * (uint32_t)p.H + ((lane & 7) ^ swz_of_row(r)) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_PER_WAVE; ++i) {
-    const int r = (wave * B_PER_WAVE + i) * 8 + lrow;
-    const int e = min(r, p.E - 1);
-    boff[i] = (uint32_t)e * (uint32_t)p.H + ((lane & 7) ^ swz_of_row(r)) * 8;
-  }
-  char* const a_dst = lds + wave * A_PER_WAVE * 1024;
-  char* const b_dst = lds + kRfAStages * A_STAGE + wave * B_PER_WAVE * 1024;
-  // copies of iteration i (i < 0: the prologue): x of step i+LA, weights of
-  // step i+LB, each when it exists
-  auto issue = [&](int i) {
-    const int ka = i + LA, kw = i + LB;
-    if (ka < nk) {
-#pragma unroll
-      for (int q = 0; q < A_PER_WAVE; ++q)
-        copy16_nt(x + ka * 64 + aoff[q], a_dst + (ka % kRfAStages) * A_STAGE + q * 1024);
-    }
-    if (kw >= 0 && kw < nk) {
-#pragma unroll
-      for (int q = 0; q < B_PER_WAVE; ++q) copy16(w + kw * 64 + boff[q], b_dst + (kw % kRfBStages) * B_STAGE + q * 1024);
-    }
-  };
-  f32x16 acc[2][NB];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
-  int slot[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) slot[kk] = ((kk * 2 + (lane >> 5)) ^ swz_of_row(lane & 15)) << 4;
-  const int arow = (lane & 31) * 128;
-  const int brow = (wave * 32 * NB + (lane & 31)) * 128;
-
-  for (int i = -LA; i < 0; ++i) issue(i);
-  for (int ks = 0; ks < nk; ++ks) {
-    // in issue order, only the copies of iteration ks-1 (x of step ks+LA-1
-    // and weights of step ks+LB-1, when they exist) were issued after the
-    // weights of step ks, and x of step ks came before those: wait until
-    // only iteration ks-1's copies are in flight; the barrier then also
-    // frees the stages read in step ks-1, which iteration ks refills
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of step ks-1 are done
-    if (ks + LA - 1 < nk)
-      wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
-    else if (ks + LB - 1 < nk)
-      wait_vmem_upto<B_PER_WAVE>();
-    else
-      wait_vmem_upto<0>();
-    __builtin_amdgcn_s_barrier();
-    issue(ks);
-    const char* sa = lds + (ks % kRfAStages) * A_STAGE;
-    const char* sb = lds + kRfAStages * A_STAGE + (ks % kRfBStages) * B_STAGE;
-    bf16x8 fa[2][2], fb[2][NB];
-    auto read = [&](int kk, bf16x8(&ra)[2], bf16x8(&rb)[NB]) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) ra[m] = *reinterpret_cast<const bf16x8*>(sa + arow + m * 32 * 128 + slot[kk]);
-#pragma unroll
-      for (int n = 0; n < NB; ++n) rb[n] = *reinterpret_cast<const bf16x8*>(sb + brow + n * 32 * 128 + slot[kk]);
-    };
-    read(0, fa[0], fb[0]);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) read(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int n = 0; n < NB; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][m], fb[kk & 1][n], acc[m][n], 0, 0, 0);
-      if (kk < 3) {
-        constexpr int NR = 2 + NB, NM = 2 * NB;
-#pragma unroll
-        for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        }
-        if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-        if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  // every copy has landed (the last wait was for all of them) and every wave
-  // is past its fragment reads: the stages become the logits tile
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __syncthreads();
-  float* const tile = reinterpret_cast<float*>(lds);
-#pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    const int e = wave * 32 * NB + n * 32 + (lane & 31);
-    if (e >= p.E) continue;
-    const float b = a.logit_bias ? a.logit_bias[e] : 0.0f;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tl = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        tile[tl * LROW + e] = acc[m][n][r] + b;
-      }
-  }
-  __syncthreads();
-  for (int tl = wave; tl < kRfTokens; tl += 4) {
-    const int t = t0 + tl;
-    if (t >= p.T) break;
-    const float* row = tile + tl * LROW;
-    if (a.logits_out) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int e = j * MOE_WAVE + lane;
-        if (e < p.E) a.logits_out[(int64_t)t * p.E + e] = row[e];
-      }
-    }
-    route_token<NJ>(a, row, t, lane);
-  }
-}
-
 // Selection: one wavefront per token.  The token's logits are the sum of its
 // nsplit partial rows (in slice order) plus logit_bias, or logits_in as
 // given; they are written to logits_out when set, kept in LDS, and routed.
@@ -1155,24 +999,7 @@ hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t s) {
 // the 128-token kernel, one workgroup per compute unit.
 static bool router_big_tiles(int64_t T, int E) { return E <= 256 && (T + kRgTokens - 1) / kRgTokens >= 64; }
 
-bool router_fused_applies(int64_t T, int E) { return E <= 256 && (T + kRfTokens - 1) / kRfTokens >= 256; }
-
-hipError_t launch_router_fused(const RouterArgs& a, hipStream_t s) {
-  if (a.p.T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.p.T + kRfTokens - 1) / kRfTokens));
-  if (a.p.E <= 128)
-    hipLaunchKernelGGL((router_fused_kernel<1>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((router_fused_kernel<2>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 int router_splits(int64_t T, int H, int E, int* sps) {
-  if (router_fused_applies(T, E)) {
-    // one K slice: the fused kernel
-    *sps = H / 64;
-    return 1;
-  }
   // enough (token tile, K slice) workgroups to fill the compute units: the
   // GEMM streams x from HBM, so its speed is the bytes in flight per CU.
   // 64-token tiles at two workgroups per CU (80 KB of LDS each, one step of

@@ -341,12 +341,10 @@ def test_layer_many_experts_and_slots(E, G, tg, k):
 def test_router_gemm_large_batches(T, H, E):
     """The router GEMM at large batch sizes (128-token tiles at one workgroup
     per compute unit, K split into slices, ragged last token tile, ragged last
-    slice, slices of one step), just below them (64-token tiles), and from 256
-    tiles of 64 tokens on (16321 tokens and more: the fused kernel, GEMM over
-    the whole K and selection in one launch, 128 or 256 expert columns, ragged
-    last tile): logits of every token of the first and last tiles and of a
-    sample in between against the oracle's dot products, and the routing of
-    the GPU logits bit-exact."""
+    slice, slices of one step, 128 or 256 expert columns) and just below them
+    (64-token tiles): logits of every token of the first and last tiles and
+    of a sample in between against the oracle's dot products, and the routing
+    of the GPU logits bit-exact."""
     shape = TEST_SHAPES["v3_small"].with_(T=T, H=H, E=E, G=8 if E % 8 == 0 else 1,
                                          topk_group=4 if E % 8 == 0 else 1)
     g = torch.Generator(device="cuda")
@@ -371,11 +369,11 @@ def test_router_gemm_large_batches(T, H, E):
 
 
 @pytest.mark.parametrize("cf", [0.0, 1.25])
-def test_fused_router_without_logits_output(cf):
-    """The fused large-batch router writes the logits only when asked: the
-    selection is the same with and without a logits output, and (unlimited
-    routing) bit-exact with the oracle run on the GPU's logits; with a
-    capacity limit the logits go to the workspace for the capacity pass."""
+def test_large_batch_router_without_logits_output(cf):
+    """At a prefill-sized batch the selection is the same with and without a
+    logits output (without one the logits live in the workspace) and
+    bit-exact with the oracle run on the GPU's logits, with and without a
+    capacity limit (Zipf-skewed logits, so experts fill)."""
     T, H, E = 16400, 1024, 256
     shape = TEST_SHAPES["v3_small"].with_(T=T, H=H, E=E, capacity_factor=cf)
     g = torch.Generator(device="cuda")
