@@ -162,7 +162,11 @@ def run_workload(shape, steps, warmup, dev):
     torch.cuda.synchronize()
     log("%s: warmup done" % shape.name)
 
-    moe.timing_enable(steps * 16)
+    # timed region: events around the layer and around the launches of the
+    # roofline kernel (gate/up) only -- events around every launch would add
+    # tens of microseconds per layer to what is measured
+    moe.timing_only("gateup_swiglu")
+    moe.timing_enable(steps * 2)
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -172,9 +176,17 @@ def run_workload(shape, steps, warmup, dev):
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
+    gu = moe.timing_read().get("gateup_swiglu")
+    log("%s: timed %d steps: %.3f ms/step" % (shape.name, steps, total_ms / steps))
+    # per-kernel breakdown: a second pass of the same steps, every launch
+    # bracketed (not part of the timed region)
+    moe.timing_only(None)
+    moe.timing_enable(steps * 16)
+    for _ in range(steps):
+        step()
     kern = moe.timing_read()
     moe.timing_enable(0)
-    log("%s: timed %d steps: %.3f ms/step" % (shape.name, steps, total_ms / steps))
+    torch.cuda.synchronize()
 
     assigned = int((idx >= 0).sum().item())
     touched = int((counts > 0).sum().item())
@@ -183,6 +195,7 @@ def run_workload(shape, steps, warmup, dev):
     if shape.dtype == "fp8":  # plus the UE8M0 block scales
         per_expert += 3 * (shape.H // 128) * (shape.I // 128)
     return {"inp": inp, "ms_step": total_ms / steps, "kernels": {name: ms / n for name, (ms, n) in kern.items()},
+            "gateup_ms": gu[0] / gu[1] if gu else None,
             "assigned": assigned, "touched": touched, "weight_bytes": (touched + shape.S) * per_expert,
             "gateup_weight_bytes": (touched + shape.S) * per_expert * 2 // 3,
             "down_weight_bytes": (touched + shape.S) * per_expert // 3}
@@ -306,7 +319,7 @@ def main():
     layer_flops = shape.flops(r["assigned"])
     ms_step = r["ms_step"]
     kernels = r["kernels"]
-    gu_ms = kernels.get("gateup_swiglu")
+    gu_ms = r["gateup_ms"]  # launches inside the timed region
     achieved = gateup_flops / (gu_ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if shape.dtype == "fp8" else PEAK_BF16_TFLOPS
     res = {
@@ -334,7 +347,7 @@ def main():
         "layer_mfma_frac": layer_flops / (ms_step * 1e-3) / 1e12 / peak,
         "layer_weight_gbs": r["weight_bytes"] / (ms_step * 1e-3) / 1e9,
         "layer_hbm_frac": r["weight_bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "kernels_ms": kernels,
+        "kernels_ms": kernels,  # a separate pass with every launch bracketed
         "assigned_slots": r["assigned"],
         "touched_experts": r["touched"],
     }

@@ -340,6 +340,10 @@ const char* moe_version(void);
 moe_status moe_timing_enable(int32_t max_launches);
 moe_status moe_timing_read(double* ms, int64_t* launches, int32_t n_kernels);
 const char* moe_kernel_name(int32_t id);
+/* Bracket only the launches of kernel `kernel_id` (-1: every kernel, the
+ * default): two events per timed launch perturb the stream less than two per
+ * kernel of the layer (MOE_ERR_INVALID_ARG for an unknown id). */
+moe_status moe_timing_only(int32_t kernel_id);
 
 #ifdef __cplusplus
 }

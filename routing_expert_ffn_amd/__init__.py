@@ -23,7 +23,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_forward_noalloc", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8",
            "moe_quantize_fp8", "moe_balance_update", "moe_probe_mfma_bf16", "moe_probe_read", "moe_last_error",
-           "moe_version", "moe_timing_enable", "moe_timing_read", "moe_kernel_name")
+           "moe_version", "moe_timing_enable", "moe_timing_read", "moe_timing_only", "moe_kernel_name")
 
 
 class MoeError(RuntimeError):
@@ -73,7 +73,7 @@ def lib():
         for name in ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn",
                      "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_forward_hash", "moe_forward_fp8",
                      "moe_expert_ffn_fp8", "moe_quantize_fp8", "moe_balance_update", "moe_timing_enable",
-                     "moe_timing_read", "moe_probe_mfma_bf16", "moe_probe_read"):
+                     "moe_timing_read", "moe_timing_only", "moe_probe_mfma_bf16", "moe_probe_read"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [C, I64, ctypes.POINTER(SZ)]
         L.moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -96,6 +96,7 @@ def lib():
         L.moe_version.argtypes = []
         L.moe_timing_enable.argtypes = [I32]
         L.moe_timing_read.argtypes = [P, P, I32]
+        L.moe_timing_only.argtypes = [I32]
         L.moe_kernel_name.restype = ctypes.c_char_p
         L.moe_kernel_name.argtypes = [I32]
         _lib = L
@@ -329,6 +330,22 @@ def probe_read(buf, mode, blocks, sink, stream=None):
 
 def timing_enable(max_launches):
     _check(lib().moe_timing_enable(int(max_launches)))
+
+
+def timing_only(name=None):
+    """Bracket only the launches of the named kernel (None: every kernel)."""
+    kid = -1
+    if name is not None:
+        i = 0
+        while True:
+            n = lib().moe_kernel_name(i)
+            if n is None:
+                raise ValueError("unknown kernel %r" % name)
+            if n.decode() == name:
+                kid = i
+                break
+            i += 1
+    _check(lib().moe_timing_only(kid))
 
 
 def timing_read(n_kernels=16):

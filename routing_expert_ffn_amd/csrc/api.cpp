@@ -30,6 +30,7 @@ moe_status hip_fail(hipError_t e, const char* what) {
 struct Timing {
   int max = 0;
   int used = 0;
+  int only = -1;  // kernel id whose launches are bracketed, -1 = every kernel
   std::vector<hipEvent_t> ev;
   std::vector<int> ids;
 };
@@ -37,7 +38,7 @@ Timing g_timing;
 
 template <class F>
 hipError_t timed(int id, hipStream_t s, F&& f) {
-  if (g_timing.max > 0 && g_timing.used < g_timing.max) {
+  if (g_timing.max > 0 && g_timing.used < g_timing.max && (g_timing.only < 0 || g_timing.only == id)) {
     const int slot = g_timing.used++;
     hipEventRecord(g_timing.ev[2 * slot], s);
     const hipError_t err = f();
@@ -948,5 +949,11 @@ moe_status moe_timing_read(double* ms, int64_t* launches, int32_t n_kernels) {
 }
 
 const char* moe_kernel_name(int32_t id) { return kernel_name(id); }
+
+moe_status moe_timing_only(int32_t kernel_id) {
+  if (kernel_id < -1 || kernel_id >= K_COUNT) return fail(MOE_ERR_INVALID_ARG, "kernel_id must be -1 or a kernel id");
+  g_timing.only = kernel_id;
+  return MOE_OK;
+}
 
 }  // extern "C"

@@ -692,6 +692,15 @@ def test_timing_records_every_kernel():
     for name in ("router", "permute_count", "permute_scan", "permute_scatter", "schedule", "gateup_swiglu", "down",
                  "combine"):
         assert name in t and t[name][1] == 1 and t[name][0] > 0.0, name
+    # only the selected kernel's launches are bracketed
+    moe.timing_only("gateup_swiglu")
+    moe.timing_enable(64)
+    run_layer(shape, inp, "bf16")
+    run_layer(shape, inp, "bf16")
+    t = moe.timing_read()
+    moe.timing_enable(0)
+    moe.timing_only(None)
+    assert list(t) == ["gateup_swiglu"] and t["gateup_swiglu"][1] == 2 and t["gateup_swiglu"][0] > 0.0
 
 
 def test_native_library_is_the_one_loaded():
