@@ -559,6 +559,11 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   }
   g.c = y_rows;
   g.c16 = y16;
+  // at short K (I <= 4096: 32 or fewer steps per item) the h rows' copies are
+  // the ones that arrive late: three h stages and two weight stages (measured
+  // on the DeepSeek-V2/V3/V4 shapes: down 2-4 % faster; at the Mixtral
+  // shape's K = 14336 and when the weights stream once, 8-9 % slower)
+  g.a3 = d.dtype == MOE_BF16 && !g.stream_b && d.I <= 4096 ? 1 : 0;
   g.n_routed = d.E;
   g.routed_rows = (int)(d.T * d.k);
   if (bound * g.n_tiles > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "too many GEMM tiles");

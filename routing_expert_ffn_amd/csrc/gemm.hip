@@ -33,7 +33,8 @@ constexpr int kWM = 128;               // rows per wavefront (bf16 path); BM = 2
 // LDS: two A stages (input rows) and three B stages (weight rows), 32 KB
 // each, 160 KB in all.  Both operands are copied two steps ahead of use: B
 // into the stage freed one step earlier (three stages), A right after the
-// barrier that frees its stage (two stages).
+// barrier that frees its stage (two stages).  The down GEMM at short K swaps
+// the roles (gemm_tile's A3).
 constexpr int kAStage = 2 * kWM * kRowBytes;
 constexpr int kBStage = kBNB * kRowBytes;
 constexpr int kAStages = 2, kBStages = 3;
@@ -126,8 +127,12 @@ __device__ __forceinline__ void interleave_reads() {
 // expert's last row tile 3*kWM/4 when it has at most 3*kWM/2 rows and kWM/2
 // when it has at most kWM, which then costs three quarters or half of the
 // MFMAs instead of computing padding.
-template <int WM, bool GATEUP, bool NTB>
+// A3: three A stages and two B stages instead of two and three (A copied two
+// steps ahead in sub-steps 0-2, B right after the barrier that frees its
+// stage): at short K the input rows' copies are the ones that arrive late.
+template <int WM, bool GATEUP, bool NTB, bool A3 = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, int nt, int row0, int rows) {
+  constexpr int AS = A3 ? 3 : 2, BS = A3 ? 2 : 3;  // A and B stages
   constexpr int BM = 2 * WM;
   constexpr int MB = WM / 32;
   constexpr int A_PER_WAVE = BM / 8 / 4;    // 8-row groups of A each wave copies
@@ -177,7 +182,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
       boff[i] = (uint32_t)rb * (uint32_t)K + ((lane & 7) ^ swz_of_row(rb)) * 8;
     }
   }
-  char* const b_lds = lds + kAStages * kAStage;
+  char* const b_lds = lds + AS * kAStage;
   char* const a_dst = lds + wave * A_PER_WAVE * 1024;
   char* const b_dst = b_lds + wave * B_PER_WAVE * 1024;
 
@@ -206,57 +211,109 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   for (int kk = 0; kk < 4; ++kk) slot[kk] = ((kk * 2 + (lane >> 5)) ^ swz_of_row(lane & 15)) << 4;
 
   const int nk = K / kBK;
-  constexpr int BH = (B_PER_WAVE * 3 + 7) / 8, BH2 = 2 * BH;  // B copies in sub-steps 0 / 1 / 2
-  // prologue: A and B of steps 0 and 1 in the order of the main loop (B of a
-  // step before its A; indices clamped to the last step: a re-copy lands in
-  // a stage that is not read again), then wait for step 0
-  copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, 0, a_dst);
-  copy_rows<NTB, 0, B_PER_WAVE>(bbase, boff, b_dst);
-  copy_rows<NTB, 0, B_PER_WAVE>(bbase + min(1, nk - 1) * kBK, boff, b_dst + kBStage);
-  copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, min(1, nk - 1) * kRowBytes, a_dst + kAStage);
-  wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
-  __builtin_amdgcn_s_barrier();
-
-  bf16x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
-  int sbi = 0;  // B stage of step kt (kt mod 3)
-  load_frags<MB>(lds, b_lds, arow, brow, slot[0], fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* sa = lds + (kt & 1) * kAStage;
-    const char* sb = b_lds + sbi * kBStage;
-    const int sbn = sbi == kBStages - 1 ? 0 : sbi + 1;  // B stage of step kt+1
-    const int sbf = sbn == kBStages - 1 ? 0 : sbn + 1;  // B stage of step kt+2 (free)
-    const bf16* const bn = bbase + min(kt + 2, nk - 1) * kBK;
-    // sub-steps 0, 1 and 2: B of step kt+2 (3 + 3 + 2 copies) into the stage
-    // freed at the last barrier
-    load_frags<MB>(sa, sb, arow, brow, slot[1], fa1, fb1);
-    copy_rows<NTB, 0, BH>(bn, boff, b_dst + sbf * kBStage);
-    mfma_step<MB>(fa0, fb0, acc);
-    interleave_reads<MB, BH>();
-    load_frags<MB>(sa, sb, arow, brow, slot[2], fa0, fb0);
-    copy_rows<NTB, BH, BH>(bn, boff, b_dst + sbf * kBStage);
-    mfma_step<MB>(fa1, fb1, acc);
-    interleave_reads<MB, BH>();
-    load_frags<MB>(sa, sb, arow, brow, slot[3], fa1, fb1);
-    copy_rows<NTB, BH2, B_PER_WAVE - BH2>(bn, boff, b_dst + sbf * kBStage);
-    mfma_step<MB>(fa0, fb0, acc);
-    interleave_reads<MB, B_PER_WAVE - BH2>();
-    // this wave's reads of the current stages are done and A and B of step
-    // kt+1 have landed (copies complete in issue order; only B of step kt+2
-    // was issued after them); after the barrier every wave is past the
-    // current stages and sees step kt+1
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    wait_vmem_upto<B_PER_WAVE>();
+  if constexpr (A3) {
+    // prologue: A and B of steps 0 and 1 in the order of the main loop (A
+    // of a step before its B), then wait for step 0
+    constexpr int AH = (A_PER_WAVE * 3 + 7) / 8, AH2 = 2 * AH;  // A copies in sub-steps 0 / 1 / 2
+    constexpr int N1 = AH2 <= A_PER_WAVE ? AH : A_PER_WAVE - AH;
+    constexpr int I2 = AH2 <= A_PER_WAVE ? AH2 : A_PER_WAVE, N2 = A_PER_WAVE - I2;
+    copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, 0, a_dst);
+    copy_rows<NTB, 0, B_PER_WAVE>(bbase, boff, b_dst);
+    copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, min(1, nk - 1) * kRowBytes, a_dst + kAStage);
+    copy_rows<NTB, 0, B_PER_WAVE>(bbase + min(1, nk - 1) * kBK, boff, b_dst + kBStage);
+    wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // last sub-step: A of step kt+2 into the A stage just freed, and step
-    // kt+1's first fragments (after the last step: harmless reads of unused
-    // stages).  Every copy thus has a full step or more before the barrier
-    // that needs it.
-    load_frags<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, slot[0], fa0, fb0);
-    copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, min(kt + 2, nk - 1) * kRowBytes, a_dst + (kt & 1) * kAStage);
-    mfma_step<MB>(fa1, fb1, acc);
-    interleave_reads<MB, A_PER_WAVE>();
-    sbi = sbn;
+
+    bf16x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
+    int sai = 0;  // A stage of step kt (kt mod 3)
+    load_frags<MB>(lds, b_lds, arow, brow, slot[0], fa0, fb0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* sa = lds + sai * kAStage;
+      const char* sb = b_lds + (kt & 1) * kBStage;
+      const int san = sai == AS - 1 ? 0 : sai + 1;  // A stage of step kt+1
+      const int saf = san == AS - 1 ? 0 : san + 1;  // A stage of step kt+2 (free)
+      const uint32_t an = min(kt + 2, nk - 1) * kRowBytes;
+      // sub-steps 0, 1 and 2: A of step kt+2 into the stage freed at the last
+      // barrier
+      load_frags<MB>(sa, sb, arow, brow, slot[1], fa1, fb1);
+      copy_rows_buf<0, AH>(arsrc, aoff, an, a_dst + saf * kAStage);
+      mfma_step<MB>(fa0, fb0, acc);
+      interleave_reads<MB, AH>();
+      load_frags<MB>(sa, sb, arow, brow, slot[2], fa0, fb0);
+      copy_rows_buf<AH, N1>(arsrc, aoff, an, a_dst + saf * kAStage);
+      mfma_step<MB>(fa1, fb1, acc);
+      interleave_reads<MB, N1>();
+      load_frags<MB>(sa, sb, arow, brow, slot[3], fa1, fb1);
+      copy_rows_buf<I2, N2>(arsrc, aoff, an, a_dst + saf * kAStage);
+      mfma_step<MB>(fa0, fb0, acc);
+      interleave_reads<MB, N2>();
+      // this wave's reads of the current stages are done and A and B of step
+      // kt+1 have landed (only A of step kt+2 was issued after them)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      wait_vmem_upto<A_PER_WAVE>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // last sub-step: B of step kt+2 into the B stage just freed, and step
+      // kt+1's first fragments
+      load_frags<MB>(lds + san * kAStage, b_lds + ((kt + 1) & 1) * kBStage, arow, brow, slot[0], fa0, fb0);
+      copy_rows<NTB, 0, B_PER_WAVE>(bbase + min(kt + 2, nk - 1) * kBK, boff, b_dst + (kt & 1) * kBStage);
+      mfma_step<MB>(fa1, fb1, acc);
+      interleave_reads<MB, B_PER_WAVE>();
+      sai = san;
+    }
+  } else {
+    constexpr int BH = (B_PER_WAVE * 3 + 7) / 8, BH2 = 2 * BH;  // B copies in sub-steps 0 / 1 / 2
+    // prologue: A and B of steps 0 and 1 in the order of the main loop (B of a
+    // step before its A; indices clamped to the last step: a re-copy lands in
+    // a stage that is not read again), then wait for step 0
+    copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, 0, a_dst);
+    copy_rows<NTB, 0, B_PER_WAVE>(bbase, boff, b_dst);
+    copy_rows<NTB, 0, B_PER_WAVE>(bbase + min(1, nk - 1) * kBK, boff, b_dst + kBStage);
+    copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, min(1, nk - 1) * kRowBytes, a_dst + kAStage);
+    wait_vmem_upto<A_PER_WAVE + B_PER_WAVE>();
+    __builtin_amdgcn_s_barrier();
+
+    bf16x8 fa0[MB], fb0[4], fa1[MB], fb1[4];
+    int sbi = 0;  // B stage of step kt (kt mod 3)
+    load_frags<MB>(lds, b_lds, arow, brow, slot[0], fa0, fb0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* sa = lds + (kt & 1) * kAStage;
+      const char* sb = b_lds + sbi * kBStage;
+      const int sbn = sbi == BS - 1 ? 0 : sbi + 1;  // B stage of step kt+1
+      const int sbf = sbn == BS - 1 ? 0 : sbn + 1;  // B stage of step kt+2 (free)
+      const bf16* const bn = bbase + min(kt + 2, nk - 1) * kBK;
+      // sub-steps 0, 1 and 2: B of step kt+2 (3 + 3 + 2 copies) into the stage
+      // freed at the last barrier
+      load_frags<MB>(sa, sb, arow, brow, slot[1], fa1, fb1);
+      copy_rows<NTB, 0, BH>(bn, boff, b_dst + sbf * kBStage);
+      mfma_step<MB>(fa0, fb0, acc);
+      interleave_reads<MB, BH>();
+      load_frags<MB>(sa, sb, arow, brow, slot[2], fa0, fb0);
+      copy_rows<NTB, BH, BH>(bn, boff, b_dst + sbf * kBStage);
+      mfma_step<MB>(fa1, fb1, acc);
+      interleave_reads<MB, BH>();
+      load_frags<MB>(sa, sb, arow, brow, slot[3], fa1, fb1);
+      copy_rows<NTB, BH2, B_PER_WAVE - BH2>(bn, boff, b_dst + sbf * kBStage);
+      mfma_step<MB>(fa0, fb0, acc);
+      interleave_reads<MB, B_PER_WAVE - BH2>();
+      // this wave's reads of the current stages are done and A and B of step
+      // kt+1 have landed (copies complete in issue order; only B of step kt+2
+      // was issued after them); after the barrier every wave is past the
+      // current stages and sees step kt+1
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      wait_vmem_upto<B_PER_WAVE>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // last sub-step: A of step kt+2 into the A stage just freed, and step
+      // kt+1's first fragments (after the last step: harmless reads of unused
+      // stages).  Every copy thus has a full step or more before the barrier
+      // that needs it.
+      load_frags<MB>(lds + ((kt + 1) & 1) * kAStage, b_lds + sbn * kBStage, arow, brow, slot[0], fa0, fb0);
+      copy_rows_buf<0, A_PER_WAVE>(arsrc, aoff, min(kt + 2, nk - 1) * kRowBytes, a_dst + (kt & 1) * kAStage);
+      mfma_step<MB>(fa1, fb1, acc);
+      interleave_reads<MB, A_PER_WAVE>();
+      sbi = sbn;
+    }
   }
   // no copy may still be writing LDS when the stages are reused or released
   wait_vmem_upto<0>();
@@ -328,7 +385,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
 }
 
 // NTB: the weights are read with the non-temporal policy (each is read once).
-template <bool GATEUP, bool NTB>
+template <bool GATEUP, bool NTB, bool A3>
 __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   Work w;
@@ -337,14 +394,14 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
     // an expert's last row tile of 129-192 rows runs three 32-row blocks per
     // wavefront instead of four (a quarter less MFMA work on padding rows)
     if (w.rows > 3 * kWM / 2)
-      gemm_tile<kWM, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile<kWM, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
     else
-      gemm_tile<3 * kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile<3 * kWM / 4, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
   } else {
-    gemm_tile<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
+    gemm_tile<kWM / 2, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();  // every wave is past its last reads of the LDS stages
-      gemm_tile<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+      gemm_tile<kWM / 2, GATEUP, NTB, A3>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
     }
   }
 }
@@ -467,9 +524,9 @@ hipError_t launch_gateup(const GemmArgs& a, int dtype, int64_t mtile_bound, hipS
   if (dtype != 1) {
     hipLaunchKernelGGL((expert_gemm_f32<true>), dim3((unsigned)grid), dim3(64), 0, s, a);
   } else if (a.stream_b) {
-    hipLaunchKernelGGL((expert_gemm_bf16<true, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<true, true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((expert_gemm_bf16<true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<true, false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -481,9 +538,11 @@ hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStr
   if (dtype != 1) {
     hipLaunchKernelGGL((expert_gemm_f32<false>), dim3((unsigned)grid), dim3(64), 0, s, a);
   } else if (a.stream_b) {
-    hipLaunchKernelGGL((expert_gemm_bf16<false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<false, true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  } else if (a.a3) {
+    hipLaunchKernelGGL((expert_gemm_bf16<false, false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((expert_gemm_bf16<false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<false, false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -125,6 +125,8 @@ struct GemmArgs {
   // 1: every expert has at most one row tile, so each weight tile is read by
   // one item only and the weight copies take the non-temporal policy
   int stream_b;
+  // bf16 down GEMM: 1 = three stages of input rows and two of weights
+  int a3;
 };
 
 // Weight scales repacked with rows padded to 4 bytes (three matrices).
