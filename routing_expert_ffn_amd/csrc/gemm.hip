@@ -96,12 +96,16 @@ __device__ __forceinline__ void mfma_step(const bf16x8 (&fa)[MB], const bf16x8 (
 // address unit and stalls the wave's in-order issue, MFMAs included.
 template <int MB, int NC>
 __device__ __forceinline__ void interleave_reads() {
-  constexpr int NR = MB + 4, NM = MB * 4 - NR;  // MFMAs left after the reads
+  // NR fragment reads against MB*4 MFMAs: one read after each MFMA while both
+  // last (a one-block tile has one more read than MFMAs), then the copies
+  constexpr int NR = MB + 4, NP = NR < MB * 4 ? NR : MB * 4;
+  constexpr int NM = MB * 4 - NP;  // MFMAs left after the reads
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
+  for (int i = 0; i < NP; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
   }
+  if (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
@@ -124,9 +128,9 @@ __device__ __forceinline__ void interleave_reads() {
 
 // One output tile: rows [row0, row0 + rows) of expert e, column tile nt.  WM
 // is the row count per wavefront: kWM for a full tile (2*kWM rows); for an
-// expert's last row tile 3*kWM/4 when it has at most 3*kWM/2 rows and kWM/2
-// when it has at most kWM, which then costs three quarters or half of the
-// MFMAs instead of computing padding.
+// expert's last row tile 3*kWM/4 when it has at most 3*kWM/2 rows, kWM/2 when
+// it has at most kWM and kWM/4 when it has at most kWM/2, which then costs
+// three quarters, half or a quarter of the MFMAs instead of computing padding.
 // A3: three A stages and two B stages instead of two and three (A copied two
 // steps ahead in sub-steps 0-2, B right after the barrier that frees its
 // stage): at short K the input rows' copies are the ones that arrive late.
@@ -397,11 +401,18 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
       gemm_tile<kWM, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
     else
       gemm_tile<3 * kWM / 4, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
-  } else {
+  } else if (w.rows > kWM / 2) {
     gemm_tile<kWM / 2, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();  // every wave is past its last reads of the LDS stages
       gemm_tile<kWM / 2, GATEUP, NTB, A3>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+    }
+  } else {
+    // a short tile of at most 64 rows: one 32-row block per wavefront
+    gemm_tile<kWM / 4, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
+    if (w.nt + 1 < a.n_tiles) {
+      __syncthreads();
+      gemm_tile<kWM / 4, GATEUP, NTB, A3>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
     }
   }
 }
@@ -500,7 +511,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(ScheduleArgs a) {
 }  // namespace
 
 // tile geometry per input dtype: fp32 (0) 32-row tiles; bf16 (1) and FP8
-// experts (2) 256-row tiles with half-height last tiles
+// experts (2) 256-row tiles with half- or quarter-height last tiles
 int gemm_bm(int dtype) { return dtype != 0 ? 2 * kWM : 32; }
 
 int gemm_half_rows(int dtype) { return dtype != 0 ? kWM : 0; }

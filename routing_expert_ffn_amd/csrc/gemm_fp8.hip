@@ -127,18 +127,21 @@ __device__ __forceinline__ void mfma_step8(const i32x8 (&fa)[MB], const i32x8 (&
 }
 
 // Interleave one sub-step: NS scale loads first, two fragment reads after
-// each of the first MB+4 MFMAs, then the NC copies one per MFMA (reads are
-// written before copies in program order, which the compiler keeps for LDS
-// reads and LDS copies).
+// each of the first MB+4 MFMAs (a one-block tile has one fragment more than
+// MFMAs: its last two reads follow), then the NC copies one per MFMA (reads
+// are written before copies in program order, which the compiler keeps for
+// LDS reads and LDS copies).
 template <int MB, int NC, int NS = 0>
 __device__ __forceinline__ void interleave8() {
-  constexpr int NR = MB + 4, NM = MB * 4 - NR;
+  constexpr int NR = MB + 4, NP = NR < MB * 4 ? NR : MB * 4;
+  constexpr int NM = MB * 4 - NP;
   if (NS > 0) __builtin_amdgcn_sched_group_barrier(0x020, NS, 0);  // scale loads
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
+  for (int i = 0; i < NP; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
   }
+  if (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (NR - NP), 0);
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -445,11 +448,18 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_fp8(GemmArgs a) {
       gemm_tile_fp8<kWM, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
     else
       gemm_tile_fp8<3 * kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
-  } else {
+  } else if (w.rows > kWM / 2) {
     gemm_tile_fp8<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();
       gemm_tile_fp8<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+    }
+  } else {
+    // a short tile of at most 64 rows: one 32-row block per wavefront
+    gemm_tile_fp8<kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
+    if (w.nt + 1 < a.n_tiles) {
+      __syncthreads();
+      gemm_tile_fp8<kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
     }
   }
 }

@@ -13,7 +13,9 @@ constexpr int kGroup = 4;             // full row tiles of an expert walked toge
 // of up to kGroup full row tiles; inside a group, column-tile pairs (2p, 2p+1),
 // first every full row tile of the group at column 2p, then at 2p+1, then --
 // in the expert's last group only -- one item that runs the expert's short
-// last row tile (at most half_rows rows, half the MFMA work) at both columns.
+// last row tile (at most half_rows rows: half the MFMA work, a quarter when it
+// has at most half_rows/2 rows and the kernel runs quarter-height tiles) at
+// both columns.
 // Every item then takes about one full tile's time, items that share a weight
 // tile or a row tile of the input are close together, and each XCD (one L2)
 // walks a contiguous range of items, so neighbours run at the same time and
