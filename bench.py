@@ -222,7 +222,8 @@ def decode_record(shape, r):
 def attainable_rates(dev, mfma_seconds=1.2):
     """Sustained bf16 MFMA rate (about mfma_seconds of back-to-back launches;
     operands that change between instructions, as in a GEMM, and for
-    comparison one fixed operand pair) and HBM streaming read rate of this
+    comparison one fixed operand pair), the same for the FP8 experts' scaled
+    E4M3 instruction (varying operands), and HBM streaming read rate of this
     GPU, from the library's probe kernels."""
     import torch
 
@@ -244,16 +245,18 @@ def attainable_rates(dev, mfma_seconds=1.2):
         return a.elapsed_time(b) / n
 
     out = {}
-    for vary, key in ((True, "mfma_bf16_tflops"), (False, "mfma_bf16_tflops_fixed_operands")):
+    for probe, vary, key in ((moe.probe_mfma_bf16, True, "mfma_bf16_tflops"),
+                             (moe.probe_mfma_bf16, False, "mfma_bf16_tflops_fixed_operands"),
+                             (moe.probe_mfma_fp8, True, "mfma_fp8_tflops")):
         # size one launch to about a quarter of the target, then time four
         iters = 20000
-        ms = timed(lambda: moe.probe_mfma_bf16(blocks, iters, sink, vary=vary), 1)
+        ms = timed(lambda: probe(blocks, iters, sink, vary=vary), 1)
         iters = max(1, int(iters * (mfma_seconds * 250.0) / ms))
-        flops = moe.probe_mfma_bf16(blocks, iters, sink, vary=vary)
-        ms = timed(lambda: moe.probe_mfma_bf16(blocks, iters, sink, vary=vary), 4)
+        flops = probe(blocks, iters, sink, vary=vary)
+        ms = timed(lambda: probe(blocks, iters, sink, vary=vary), 4)
         out[key] = flops / (ms * 1e-3) / 1e12
-        log("probe: bf16 MFMA %.0f TFLOP/s sustained, %s operands (4 launches of %.0f ms)"
-            % (out[key], "varying" if vary else "fixed", ms))
+        log("probe: %s MFMA %.0f TFLOP/s sustained, %s operands (4 launches of %.0f ms)"
+            % ("fp8" if probe is moe.probe_mfma_fp8 else "bf16", out[key], "varying" if vary else "fixed", ms))
     out["mfma_seconds"] = 5 * ms * 1e-3
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -372,9 +375,10 @@ def main():
 
     if not args.no_peaks:
         att = attainable_rates(dev)
-        if shape.dtype == "bf16":
-            att["layer_frac_of_attainable_mfma"] = res["layer_tflops"] / att["mfma_bf16_tflops"]
-            att["gateup_frac_of_attainable_mfma"] = achieved / att["mfma_bf16_tflops"]
+        if shape.dtype in ("bf16", "fp8"):
+            rate = att["mfma_fp8_tflops" if shape.dtype == "fp8" else "mfma_bf16_tflops"]
+            att["layer_frac_of_attainable_mfma"] = res["layer_tflops"] / rate
+            att["gateup_frac_of_attainable_mfma"] = achieved / rate
         if "decode" in res:
             att["decode_frac_of_attainable_hbm"] = res["decode"]["weight_gbs"] / att["hbm_read_gbs"]
         res["attainable"] = att

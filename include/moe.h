@@ -315,6 +315,9 @@ moe_status moe_balance_update(const moe_config* cfg, const int32_t* expert_count
  *   fragments in turn (inputs change between instructions, as in a GEMM),
  *   vary = 0 one fixed pair; *flops (host) gets the FLOPs the launch
  *   performs (blocks * iters * 4 * 8 * 32768).
+ * moe_probe_mfma_fp8: the same with v_mfma_scale_f32_32x32x64_f8f6f4 (the
+ *   FP8 expert GEMMs' instruction) on pseudo-random E4M3 operands with unit
+ *   block scales; *flops = blocks * iters * 4 * 8 * 131072.
  * moe_probe_read: reads the `bytes` (a positive multiple of 16) of the
  *   16-byte aligned device buffer `buf` once, in 16-byte pieces with eight in
  *   flight per lane, over `blocks` workgroups of 256 threads; mode 0: plain
@@ -323,6 +326,8 @@ moe_status moe_balance_update(const moe_config* cfg, const int32_t* expert_count
  *   non-temporal policy. */
 moe_status moe_probe_mfma_bf16(int32_t vary, int32_t blocks, int64_t iters, float* sink, double* flops,
                                void* stream);
+moe_status moe_probe_mfma_fp8(int32_t vary, int32_t blocks, int64_t iters, float* sink, double* flops,
+                              void* stream);
 moe_status moe_probe_read(int32_t mode, int32_t blocks, const void* buf, size_t bytes, float* sink, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */

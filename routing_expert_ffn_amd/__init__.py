@@ -22,7 +22,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_forward_noalloc", "moe_forward_hash", "moe_forward_fp8", "moe_expert_ffn_fp8",
-           "moe_quantize_fp8", "moe_balance_update", "moe_probe_mfma_bf16", "moe_probe_read", "moe_last_error",
+           "moe_quantize_fp8", "moe_balance_update", "moe_probe_mfma_bf16", "moe_probe_mfma_fp8", "moe_probe_read",
+           "moe_last_error",
            "moe_version", "moe_timing_enable", "moe_timing_read", "moe_timing_only", "moe_kernel_name")
 
 
@@ -73,7 +74,8 @@ def lib():
         for name in ("moe_workspace_size", "moe_route", "moe_route_hash", "moe_permute", "moe_expert_ffn",
                      "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_forward_hash", "moe_forward_fp8",
                      "moe_expert_ffn_fp8", "moe_quantize_fp8", "moe_balance_update", "moe_timing_enable",
-                     "moe_timing_read", "moe_timing_only", "moe_probe_mfma_bf16", "moe_probe_read"):
+                     "moe_timing_read", "moe_timing_only", "moe_probe_mfma_bf16", "moe_probe_mfma_fp8",
+                     "moe_probe_read"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [C, I64, ctypes.POINTER(SZ)]
         L.moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -89,6 +91,7 @@ def lib():
         L.moe_expert_ffn_fp8.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_quantize_fp8.argtypes = [I64, I32, P, P, P, I32, P]
         L.moe_probe_mfma_bf16.argtypes = [I32, I32, I64, P, ctypes.POINTER(ctypes.c_double), P]
+        L.moe_probe_mfma_fp8.argtypes = [I32, I32, I64, P, ctypes.POINTER(ctypes.c_double), P]
         L.moe_probe_read.argtypes = [I32, I32, P, SZ, P, P]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
@@ -314,6 +317,16 @@ def probe_mfma_bf16(blocks, iters, sink, vary=True, stream=None):
     f = ctypes.c_double(0.0)
     _check(lib().moe_probe_mfma_bf16(1 if vary else 0, int(blocks), int(iters), _p(sink), ctypes.byref(f),
                                      _stream(stream)))
+    return f.value
+
+
+def probe_mfma_fp8(blocks, iters, sink, vary=True, stream=None):
+    """The same probe on the FP8 experts' scaled E4M3 matrix instruction.
+    -> FLOPs of the launch."""
+    assert sink.dtype == torch.float32 and sink.numel() >= blocks * 256
+    f = ctypes.c_double(0.0)
+    _check(lib().moe_probe_mfma_fp8(1 if vary else 0, int(blocks), int(iters), _p(sink), ctypes.byref(f),
+                                    _stream(stream)))
     return f.value
 
 

@@ -888,15 +888,25 @@ moe_status moe_balance_update(const moe_config* cfg, const int32_t* expert_count
   return MOE_OK;
 }
 
-moe_status moe_probe_mfma_bf16(int32_t vary, int32_t blocks, int64_t iters, float* sink, double* flops,
-                               void* stream) {
+static moe_status probe_mfma(int fp8, int32_t vary, int32_t blocks, int64_t iters, float* sink, double* flops,
+                             void* stream) {
   if (vary != 0 && vary != 1) return fail(MOE_ERR_INVALID_ARG, "vary must be 0 or 1");
   if (blocks < 1 || blocks > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "blocks must be in [1, 2^20]");
   if (iters < 1) return fail(MOE_ERR_INVALID_ARG, "iters must be >= 1");
   if (!sink || !flops) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
-  *flops = (double)blocks * (double)iters * probe_mfma_flops_per_iter_block();
-  const hipError_t e = launch_probe_mfma(vary, blocks, iters, sink, static_cast<hipStream_t>(stream));
+  *flops = (double)blocks * (double)iters * probe_mfma_flops_per_iter_block(fp8);
+  const hipError_t e = launch_probe_mfma(fp8, vary, blocks, iters, sink, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "MFMA probe launch");
+}
+
+moe_status moe_probe_mfma_bf16(int32_t vary, int32_t blocks, int64_t iters, float* sink, double* flops,
+                               void* stream) {
+  return probe_mfma(0, vary, blocks, iters, sink, flops, stream);
+}
+
+moe_status moe_probe_mfma_fp8(int32_t vary, int32_t blocks, int64_t iters, float* sink, double* flops,
+                              void* stream) {
+  return probe_mfma(1, vary, blocks, iters, sink, flops, stream);
 }
 
 moe_status moe_probe_read(int32_t mode, int32_t blocks, const void* buf, size_t bytes, float* sink, void* stream) {

@@ -232,9 +232,9 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, int out_dtype, hipStr
 // Attainable-rate probes (probe.hip): threads per block, FLOPs of one loop
 // iteration of one block of the MFMA probe, and the launches.
 int probe_threads();
-double probe_mfma_flops_per_iter_block();
+double probe_mfma_flops_per_iter_block(int fp8);
 // vary: four A and four B fragments in turn (1) or one fixed pair (0)
-hipError_t launch_probe_mfma(int vary, int blocks, int64_t iters, float* sink, hipStream_t s);
+hipError_t launch_probe_mfma(int fp8, int vary, int blocks, int64_t iters, float* sink, hipStream_t s);
 // mode 0: plain loads, 1: non-temporal loads, 2: global->LDS copies, 3: the
 // same with the non-temporal policy
 hipError_t launch_probe_read(int mode, int blocks, const void* buf, int64_t n16, float* sink, hipStream_t s);

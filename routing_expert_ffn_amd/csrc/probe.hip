@@ -11,6 +11,9 @@
 //   fragments taken in turn (the realistic case: the multiplier inputs
 //   change between instructions, as in a GEMM), or one fixed pair (far fewer
 //   toggling bits, less power, a higher clock under the power limit).
+// mfma_fp8_probe_kernel: the same with v_mfma_scale_f32_32x32x64_f8f6f4 on
+//   E4M3 operands and unit block scales, the instruction of the FP8 expert
+//   GEMMs.
 // read_probe_kernel: a grid-stride read of a device buffer in 16-byte pieces,
 //   eight loads in flight per lane, into registers with the default or the
 //   non-temporal cache policy, or as global->LDS copies with either policy
@@ -20,6 +23,8 @@
 #include "kernels.hpp"
 
 namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kProbeThreads = 256;
 constexpr int kMfmaChains = 8;
@@ -59,6 +64,48 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int64_t iters
     for (int c = 0; c < kMfmaChains; ++c) {
       const int fa = VARY ? (c & 3) : 0, fb = VARY ? ((c + (c >> 2)) & 3) : 0;
       acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fa], b[fb], acc[c], 0, 0, 0);
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[tid] = s;
+}
+
+// Four pseudo-random E4M3 codes in a dword; bit 3 of each byte cleared, so
+// no code is the NaN pattern (0x7F / 0xFF).
+__device__ __forceinline__ int probe_fp8x4(uint32_t a, uint32_t b) {
+  uint32_t h = a * 0x9E3779B1u ^ (b + 0x7F4A7C15u) * 0x85EBCA77u;
+  h ^= h >> 15;
+  h *= 0xC2B2AE3Du;
+  h ^= h >> 13;
+  return (int)(h & 0xF7F7F7F7u);
+}
+
+template <bool VARY>
+__global__ __launch_bounds__(kProbeThreads) void mfma_fp8_probe_kernel(int64_t iters, float* sink) {
+  const int tid = blockIdx.x * kProbeThreads + threadIdx.x;
+  i32x8 a[4], b[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[f][i] = probe_fp8x4((uint32_t)tid, (uint32_t)(f * 8 + i));
+      b[f][i] = probe_fp8x4((uint32_t)tid + 0x10000u, (uint32_t)(f * 8 + i));
+    }
+  f32x16 acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c) {
+      const int fa = VARY ? (c & 3) : 0, fb = VARY ? ((c + (c >> 2)) & 3) : 0;
+      // formats 0/0 (E4M3 both), scale exponent bytes 127 (x 1)
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fa], b[fb], acc[c], 0, 0, 0, 127, 0, 127);
     }
   }
   float s = 0.0f;
@@ -123,12 +170,16 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* 
 
 int probe_threads() { return kProbeThreads; }
 
-double probe_mfma_flops_per_iter_block() {
-  return (double)(kProbeThreads / 64) * kMfmaChains * 32.0 * 32.0 * 16.0 * 2.0;
+double probe_mfma_flops_per_iter_block(int fp8) {
+  return (double)(kProbeThreads / 64) * kMfmaChains * 32.0 * 32.0 * (fp8 ? 64.0 : 16.0) * 2.0;
 }
 
-hipError_t launch_probe_mfma(int vary, int blocks, int64_t iters, float* sink, hipStream_t s) {
-  if (vary)
+hipError_t launch_probe_mfma(int fp8, int vary, int blocks, int64_t iters, float* sink, hipStream_t s) {
+  if (fp8 && vary)
+    hipLaunchKernelGGL((mfma_fp8_probe_kernel<true>), dim3(blocks), dim3(kProbeThreads), 0, s, iters, sink);
+  else if (fp8)
+    hipLaunchKernelGGL((mfma_fp8_probe_kernel<false>), dim3(blocks), dim3(kProbeThreads), 0, s, iters, sink);
+  else if (vary)
     hipLaunchKernelGGL((mfma_probe_kernel<true>), dim3(blocks), dim3(kProbeThreads), 0, s, iters, sink);
   else
     hipLaunchKernelGGL((mfma_probe_kernel<false>), dim3(blocks), dim3(kProbeThreads), 0, s, iters, sink);
