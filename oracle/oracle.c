@@ -35,7 +35,11 @@
  *  - capacity C = ceil(((cf*T)*k)/E) in IEEE double, tokens served first come
  *    first served in index order, each taking its best-ranked allowed experts
  *    that still have room; slots left empty get index -1 and gate 0; groups
- *    are not re-chosen after overflow; gates are computed on the final set;
+ *    are not re-chosen after overflow; gates are computed on the final set.
+ *    Parity unpinned: the pages fix that an expert takes at most C tokens and
+ *    that overflow moves to the next-best expert (both pinned), not which
+ *    tokens are served first; the index order is checked only against a
+ *    brute-force walk written from the same reading;
  *  - drop mode (the same page's serving configuration, section 4.2: the
  *    drop_tokens switch, overflow is dropped rather than sent to a lesser
  *    expert): each token keeps its top-k and the gates of that top-k; in
