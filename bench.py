@@ -187,6 +187,9 @@ def run_workload(shape, steps, warmup, dev):
     kern = moe.timing_read()
     moe.timing_enable(0)
     torch.cuda.synchronize()
+    graph_ms, graph_same = graph_replay_ms(step, steps, out)
+    log("%s: %d replays of the layer captured in a HIP graph: %.3f ms/step (output %s)"
+        % (shape.name, steps, graph_ms, "bit-identical" if graph_same else "DIFFERENT"))
 
     assigned = int((idx >= 0).sum().item())
     touched = int((counts > 0).sum().item())
@@ -195,10 +198,45 @@ def run_workload(shape, steps, warmup, dev):
     if shape.dtype == "fp8":  # plus the UE8M0 block scales
         per_expert += 3 * (shape.H // 128) * (shape.I // 128)
     return {"inp": inp, "ms_step": total_ms / steps, "kernels": {name: ms / n for name, (ms, n) in kern.items()},
+            "ms_step_graph": graph_ms, "graph_output_identical": graph_same,
             "gateup_ms": gu[0] / gu[1] if gu else None,
             "assigned": assigned, "touched": touched, "weight_bytes": (touched + shape.S) * per_expert,
             "gateup_weight_bytes": (touched + shape.S) * per_expert * 2 // 3,
             "down_weight_bytes": (touched + shape.S) * per_expert // 3}
+
+
+def graph_replay_ms(step, steps, out):
+    """The same layer call captured once in a HIP graph (torch.cuda.CUDAGraph
+    on the library's launches) and replayed `steps` times: ms per replay, and
+    whether the replayed output equals the eager one bit for bit (the layer is
+    deterministic).  Not the headline figure: the graph removes the host's
+    launch overhead that a caller without one pays."""
+    import torch
+
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, ref))
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    same = same and bool(torch.equal(out, ref))
+    del g
+    return a.elapsed_time(b) / steps, same
 
 
 def decode_record(shape, r):
@@ -209,7 +247,8 @@ def decode_record(shape, r):
     rec = {"workload": shape.name, "tokens": shape.T, "capacity_factor": shape.capacity_factor,
            "ms_per_layer": ms, "tokens_per_s": shape.T / (ms * 1e-3), "touched_experts": r["touched"],
            "assigned_slots": r["assigned"], "weight_bytes": r["weight_bytes"], "weight_gbs": gbs,
-           "hbm_frac": gbs / PEAK_HBM_GBS, "kernels_ms": k}
+           "hbm_frac": gbs / PEAK_HBM_GBS, "kernels_ms": k,
+           "ms_per_layer_graph": r["ms_step_graph"], "graph_output_identical": r["graph_output_identical"]}
     for name, key in (("gateup_swiglu", "gateup_weight_bytes"), ("down", "down_weight_bytes")):
         if k.get(name):
             rec[name + "_weight_gbs"] = r[key] / (k[name] * 1e-3) / 1e9
@@ -351,6 +390,8 @@ def main():
         "layer_weight_gbs": r["weight_bytes"] / (ms_step * 1e-3) / 1e9,
         "layer_hbm_frac": r["weight_bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels_ms": kernels,  # a separate pass with every launch bracketed
+        "ms_per_step_graph": r["ms_step_graph"],  # the same call replayed from a HIP graph
+        "graph_output_identical": r["graph_output_identical"],
         "assigned_slots": r["assigned"],
         "touched_experts": r["touched"],
     }
