@@ -519,7 +519,8 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   g.pool = d.dtype != MOE_F32 ? sa.pool : nullptr;
   // at most BM tokens: every expert segment (a token takes an expert at most
   // once; the shared experts have T rows) fits in one row tile, so each
-  // weight tile is read by a single item and streams past the caches
+  // weight tile is read by a single item (the GEMMs stream the weights of
+  // every single-tile expert past the caches, whatever T)
   g.stream_b = d.T <= BM ? 1 : 0;
   void* h = at<void>(ws, L.h);
   // gate/up + SwiGLU

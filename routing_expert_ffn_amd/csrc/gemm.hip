@@ -388,8 +388,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
   }
 }
 
-// NTB: the weights are read with the non-temporal policy (each is read once).
-template <bool GATEUP, bool NTB, bool A3>
+// Weight cache policy.  NT = 2 (gate/up): per item -- the weights of an
+// expert whose rows fit one row tile are read by that item only and are
+// copied with the non-temporal policy (they stream past the caches), an
+// expert with several row tiles re-reads each weight tile from L2.  NT = 1:
+// every item non-temporal (launches where every expert fits one row tile);
+// NT = 0: the default policy.  (The down GEMM keeps one policy per launch:
+// with both forms of its tile in one kernel its registers spill and it runs
+// slower.)
+template <int WM, bool GATEUP, int NT, bool A3>
+__device__ __forceinline__ void gemm_tile_of(const GemmArgs& a, char* lds, const Work& w, int nt) {
+  if (NT == 1 || (NT == 2 && w.single))
+    gemm_tile<WM, GATEUP, true, A3>(a, lds, w.e, nt, w.row0, w.rows);
+  else
+    gemm_tile<WM, GATEUP, false, A3>(a, lds, w.e, nt, w.row0, w.rows);
+}
+
+template <bool GATEUP, int NT, bool A3>
 __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   Work w;
@@ -398,21 +413,21 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmArgs a) {
     // an expert's last row tile of 129-192 rows runs three 32-row blocks per
     // wavefront instead of four (a quarter less MFMA work on padding rows)
     if (w.rows > 3 * kWM / 2)
-      gemm_tile<kWM, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile_of<kWM, GATEUP, NT, A3>(a, lds, w, w.nt);
     else
-      gemm_tile<3 * kWM / 4, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile_of<3 * kWM / 4, GATEUP, NT, A3>(a, lds, w, w.nt);
   } else if (w.rows > kWM / 2) {
-    gemm_tile<kWM / 2, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
+    gemm_tile_of<kWM / 2, GATEUP, NT, A3>(a, lds, w, w.nt);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();  // every wave is past its last reads of the LDS stages
-      gemm_tile<kWM / 2, GATEUP, NTB, A3>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+      gemm_tile_of<kWM / 2, GATEUP, NT, A3>(a, lds, w, w.nt + 1);
     }
   } else {
     // a short tile of at most 64 rows: one 32-row block per wavefront
-    gemm_tile<kWM / 4, GATEUP, NTB, A3>(a, lds, w.e, w.nt, w.row0, w.rows);
+    gemm_tile_of<kWM / 4, GATEUP, NT, A3>(a, lds, w, w.nt);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();
-      gemm_tile<kWM / 4, GATEUP, NTB, A3>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+      gemm_tile_of<kWM / 4, GATEUP, NT, A3>(a, lds, w, w.nt + 1);
     }
   }
 }
@@ -534,10 +549,8 @@ hipError_t launch_gateup(const GemmArgs& a, int dtype, int64_t mtile_bound, hipS
   if (grid <= 0) return hipSuccess;
   if (dtype != 1) {
     hipLaunchKernelGGL((expert_gemm_f32<true>), dim3((unsigned)grid), dim3(64), 0, s, a);
-  } else if (a.stream_b) {
-    hipLaunchKernelGGL((expert_gemm_bf16<true, true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((expert_gemm_bf16<true, false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<true, 2, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -549,11 +562,11 @@ hipError_t launch_down(const GemmArgs& a, int dtype, int64_t mtile_bound, hipStr
   if (dtype != 1) {
     hipLaunchKernelGGL((expert_gemm_f32<false>), dim3((unsigned)grid), dim3(64), 0, s, a);
   } else if (a.stream_b) {
-    hipLaunchKernelGGL((expert_gemm_bf16<false, true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<false, 1, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   } else if (a.a3) {
-    hipLaunchKernelGGL((expert_gemm_bf16<false, false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<false, 0, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((expert_gemm_bf16<false, false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_gemm_bf16<false, 0, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

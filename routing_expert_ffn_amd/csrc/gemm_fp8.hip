@@ -436,8 +436,17 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, char* lds, int 
   }
 }
 
-// NTB: the weights are read with the non-temporal policy (each is read once).
-template <bool GATEUP, bool NTB>
+// Weight cache policy as in the bf16 kernels: NT = 2 per item (non-temporal
+// for an expert whose rows fit one row tile, gate/up), 1 every item, 0 none.
+template <int WM, bool GATEUP, int NT>
+__device__ __forceinline__ void gemm_tile_fp8_of(const GemmArgs& a, char* lds, const Work& w, int nt) {
+  if (NT == 1 || (NT == 2 && w.single))
+    gemm_tile_fp8<WM, GATEUP, true>(a, lds, w.e, nt, w.row0, w.rows);
+  else
+    gemm_tile_fp8<WM, GATEUP, false>(a, lds, w.e, nt, w.row0, w.rows);
+}
+
+template <bool GATEUP, int NT>
 __global__ __launch_bounds__(256, 1) void expert_gemm_fp8(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   Work w;
@@ -445,21 +454,21 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_fp8(GemmArgs a) {
   if (!w.pair) {
     // a last row tile of 129-192 rows: three 32-row blocks per wavefront
     if (w.rows > 3 * kWM / 2)
-      gemm_tile_fp8<kWM, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile_fp8_of<kWM, GATEUP, NT>(a, lds, w, w.nt);
     else
-      gemm_tile_fp8<3 * kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
+      gemm_tile_fp8_of<3 * kWM / 4, GATEUP, NT>(a, lds, w, w.nt);
   } else if (w.rows > kWM / 2) {
-    gemm_tile_fp8<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
+    gemm_tile_fp8_of<kWM / 2, GATEUP, NT>(a, lds, w, w.nt);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();
-      gemm_tile_fp8<kWM / 2, GATEUP, NTB>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+      gemm_tile_fp8_of<kWM / 2, GATEUP, NT>(a, lds, w, w.nt + 1);
     }
   } else {
     // a short tile of at most 64 rows: one 32-row block per wavefront
-    gemm_tile_fp8<kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt, w.row0, w.rows);
+    gemm_tile_fp8_of<kWM / 4, GATEUP, NT>(a, lds, w, w.nt);
     if (w.nt + 1 < a.n_tiles) {
       __syncthreads();
-      gemm_tile_fp8<kWM / 4, GATEUP, NTB>(a, lds, w.e, w.nt + 1, w.row0, w.rows);
+      gemm_tile_fp8_of<kWM / 4, GATEUP, NT>(a, lds, w, w.nt + 1);
     }
   }
 }
@@ -539,22 +548,17 @@ hipError_t launch_row_scales(const RowScaleArgs& a, hipStream_t s) {
 hipError_t launch_gateup_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s) {
   const int64_t grid = mtile_bound * a.n_tiles;
   if (grid <= 0) return hipSuccess;
-  if (a.stream_b) {
-    hipLaunchKernelGGL((expert_gemm_fp8<true, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((expert_gemm_fp8<true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  }
+  hipLaunchKernelGGL((expert_gemm_fp8<true, 2>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_fp8(const GemmArgs& a, int64_t mtile_bound, hipStream_t s) {
   const int64_t grid = mtile_bound * a.n_tiles;
   if (grid <= 0) return hipSuccess;
-  if (a.stream_b) {
-    hipLaunchKernelGGL((expert_gemm_fp8<false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((expert_gemm_fp8<false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  }
+  if (a.stream_b)
+    hipLaunchKernelGGL((expert_gemm_fp8<false, 1>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((expert_gemm_fp8<false, 0>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ constexpr int kGroup = 4;             // full row tiles of an expert walked toge
 // re-read shared operands from L2.
 struct Work {
   int e, nt, row0, rows;
-  bool pair;  // short row tile at columns nt and nt + 1 (when nt + 1 exists)
+  bool pair;    // short row tile at columns nt and nt + 1 (when nt + 1 exists)
+  bool single;  // the expert's rows fit one row tile: its weight tiles are read by this item only
 };
 
 __device__ __forceinline__ int items_before(const GemmArgs& a, int e, int np) {
@@ -107,6 +108,7 @@ __device__ __forceinline__ bool work_of_block(const GemmArgs& a, int BM, Work& w
   const int ncols = 2 * p + 1 < ntn ? 2 : 1;
   const int len = a.seg_len[e];
   w.e = e;
+  w.single = __builtin_amdgcn_readfirstlane(F + Hs == 1 ? 1 : 0) != 0;
   if (j < f * ncols) {
     const int mt = g * kGroup + j % f;
     w.nt = 2 * p + j / f;

@@ -123,7 +123,8 @@ struct GemmArgs {
   // launch; null: every item stays with its XCD
   int32_t* pool;
   // 1: every expert has at most one row tile, so each weight tile is read by
-  // one item only and the weight copies take the non-temporal policy
+  // one item only (the kernels choose the weights' cache policy per item,
+  // from the item's expert; this flag only selects the down GEMM's stages)
   int stream_b;
   // bf16 down GEMM: 1 = three stages of input rows and two of weights
   int a3;

@@ -228,11 +228,14 @@ def test_expert_ffn_stage_rows():
 
 @pytest.mark.parametrize("fp8", [False, True])
 def test_weight_stream_policy_is_bit_identical(fp8):
-    """At most 256 tokens the expert GEMMs copy the weights with the
-    non-temporal cache policy, above that with the default one; a cache hint
-    only, so the rows of 256 tokens come out bit-identical when a 257th token
-    is appended (its rows go to the end of every expert segment, the earlier
-    rows keep their row tiles and their K order)."""
+    """The expert GEMMs copy the weights of an expert whose rows fit one row
+    tile with the non-temporal cache policy (gate/up: per item; down: when
+    every expert does, i.e. at most 256 tokens) and the others with the
+    default one.  A cache hint only: the rows of 256 tokens come out
+    bit-identical when a 257th token is appended (its rows go to the end of
+    every expert segment, the earlier rows keep their row tiles and their K
+    order), which moves the shared expert to two row tiles and the down GEMM
+    to the default policy."""
     base = TEST_SHAPES["v3_fp8_small" if fp8 else "v3_small"]
     shape = base.with_(T=257)
     inp = make_inputs(shape, device="cuda")
