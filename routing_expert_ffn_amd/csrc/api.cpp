@@ -517,11 +517,8 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   // bf16 and FP8 kernels share each GEMM's last items between the XCDs
   // (the fp32 kernel has no LDS to broadcast the counter)
   g.pool = d.dtype != MOE_F32 ? sa.pool : nullptr;
-  // at most BM tokens: every expert segment (a token takes an expert at most
-  // once; the shared experts have T rows) fits in one row tile, so each
-  // weight tile is read by a single item (the GEMMs stream the weights of
-  // every single-tile expert past the caches, whatever T)
-  g.stream_b = d.T <= BM ? 1 : 0;
+  // (the gate/up GEMM chooses the weights' cache policy per item, from the
+  // item's expert; the down GEMM per launch, below)
   void* h = at<void>(ws, L.h);
   // gate/up + SwiGLU
   g.K = d.H;
@@ -560,6 +557,15 @@ moe_status do_ffn(const Dims& d, const void* x, const void* w_gate, const void* 
   }
   g.c = y_rows;
   g.c16 = y16;
+  // the down GEMM's weights stream past the caches (non-temporal copies)
+  // when each weight tile is read by one item: at most BM tokens (every
+  // expert segment fits one row tile: a token takes an expert at most once,
+  // a shared expert has T rows), or, for bf16 weights, when the routed
+  // experts average at most BM/2 rows (most fit one row tile; the shared
+  // experts' tiles are then re-read from HBM, measured cheaper than sending
+  // the routed weights through the caches: V3 shape down 1.43 -> 1.27 ms at
+  // 512 tokens, 1.84 -> 1.80 ms at 4096; for FP8 weights it was slower)
+  g.stream_b = d.T <= BM || (d.dtype == MOE_BF16 && d.T * d.k <= (int64_t)(BM / 2) * d.E) ? 1 : 0;
   // at short K (I <= 4096: 32 or fewer steps per item) the h rows' copies are
   // the ones that arrive late: three h stages and two weight stages (measured
   // on the DeepSeek-V2/V3/V4 shapes: down 2-4 % faster; at the Mixtral

@@ -122,9 +122,9 @@ struct GemmArgs {
   // range, taken by whichever XCD gets there first), zeroed before the
   // launch; null: every item stays with its XCD
   int32_t* pool;
-  // 1: every expert has at most one row tile, so each weight tile is read by
-  // one item only (the kernels choose the weights' cache policy per item,
-  // from the item's expert; this flag only selects the down GEMM's stages)
+  // down GEMM: 1 = its weights are copied with the non-temporal policy (each
+  // weight tile read once, or mostly once); the gate/up GEMM chooses the
+  // policy per item, from the item's expert, and ignores this field
   int stream_b;
   // bf16 down GEMM: 1 = three stages of input rows and two of weights
   int a3;

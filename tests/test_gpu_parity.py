@@ -227,22 +227,26 @@ def test_expert_ffn_stage_rows():
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-def test_weight_stream_policy_is_bit_identical(fp8):
+@pytest.mark.parametrize("T0", [256, 4096])
+def test_weight_stream_policy_is_bit_identical(fp8, T0):
     """The expert GEMMs copy the weights of an expert whose rows fit one row
-    tile with the non-temporal cache policy (gate/up: per item; down: when
-    every expert does, i.e. at most 256 tokens) and the others with the
-    default one.  A cache hint only: the rows of 256 tokens come out
-    bit-identical when a 257th token is appended (its rows go to the end of
+    tile with the non-temporal cache policy (gate/up: per item; down: per
+    launch, when every expert fits one row tile -- at most 256 tokens -- or,
+    bf16, when the routed experts average at most 128 rows) and the others
+    with the default one.  A cache hint only: the rows of T0 tokens come out
+    bit-identical when one more token is appended (its rows go to the end of
     every expert segment, the earlier rows keep their row tiles and their K
-    order), which moves the shared expert to two row tiles and the down GEMM
-    to the default policy."""
+    order).  At 256 -> 257 the shared expert moves to two row tiles (and the
+    FP8 down GEMM to the default policy); at 4096 -> 4097 (256 experts,
+    top-8: T*k passes 128*E) the bf16 down GEMM does, and expert segments of
+    128 rows move to the next tile height."""
     base = TEST_SHAPES["v3_fp8_small" if fp8 else "v3_small"]
-    shape = base.with_(T=257)
+    shape = base.with_(T=T0 + 1)
     inp = make_inputs(shape, device="cuda")
     rng = np.random.default_rng(11)
-    idx_all = np.stack([rng.permutation(shape.E)[:shape.k] for _ in range(257)]).astype(np.int32)
+    idx_all = np.stack([rng.permutation(shape.E)[:shape.k] for _ in range(T0 + 1)]).astype(np.int32)
     ys, srs = [], []
-    for T in (256, 257):
+    for T in (T0, T0 + 1):
         cfg = moe.make_config(shape.with_(T=T))
         x = inp["x"][:T].contiguous()
         _, offsets, row_token, slot_row = moe.permute(cfg, torch.from_numpy(idx_all[:T]).cuda())
@@ -255,10 +259,10 @@ def test_weight_stream_policy_is_bit_identical(fp8):
         ys.append(y.float().cpu().numpy())
         srs.append(slot_row.cpu().numpy())
     k = shape.k
-    a = ys[0][srs[0][:256].ravel()]
-    b = ys[1][srs[1][:256].ravel()]
+    a = ys[0][srs[0][:T0].ravel()]
+    b = ys[1][srs[1][:T0].ravel()]
     assert np.array_equal(a, b)
-    assert np.array_equal(ys[0][256 * k:256 * k + 256], ys[1][257 * k:257 * k + 256])   # shared expert rows
+    assert np.array_equal(ys[0][T0 * k:T0 * k + T0], ys[1][(T0 + 1) * k:(T0 + 1) * k + T0])   # shared expert rows
 
 
 def test_expert_ffn_gathers_x_up_to_2gib():
