@@ -326,6 +326,8 @@ def main():
     ap.add_argument("--capacity-factor", type=float, default=None,
                     help="override the workload's capacity factor (<= 0: unlimited)")
     ap.add_argument("--drop-tokens", action="store_true", help="with a capacity: drop the overflow")
+    ap.add_argument("--sweep-tokens", default="",
+                    help="comma-separated batch sizes: the main workload's layer at each, as a 'sweep' record")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy 1 GiB device-to-device 3 times first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -406,6 +408,24 @@ def main():
         res["cpu_baseline"] = None
     del r
     torch.cuda.empty_cache()
+
+    if args.sweep_tokens:
+        res["sweep"] = []
+        for t in [int(v) for v in args.sweep_tokens.split(",") if v]:
+            sshape = shape.with_(name="%s_T%d" % (shape.name, t), T=t)
+            d = run_workload(sshape, args.steps, args.warmup, dev)
+            ms = d["ms_step"]
+            fl = sshape.flops(d["assigned"])
+            res["sweep"].append({
+                "tokens": t, "ms_per_layer": ms, "tokens_per_s": t / (ms * 1e-3),
+                "layer_tflops": fl / (ms * 1e-3) / 1e12, "layer_mfma_frac": fl / (ms * 1e-3) / 1e12 / peak,
+                "weight_gbs": d["weight_bytes"] / (ms * 1e-3) / 1e9,
+                "hbm_frac": d["weight_bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "touched_experts": d["touched"], "assigned_slots": d["assigned"],
+                "gateup_ms": d["kernels"].get("gateup_swiglu"), "down_ms": d["kernels"].get("down")})
+            log("sweep T=%d: %.3f ms, %.0f tokens/s" % (t, ms, t / (ms * 1e-3)))
+            del d
+            torch.cuda.empty_cache()
 
     if args.decode_workload and args.decode_workload != shape.name:
         dshape = CONFIGS[args.decode_workload]
