@@ -52,10 +52,16 @@ def _tile_rows(off, T, k, E, S):
     return np.array(out, dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["deepseek_v3_prefill", "deepseek_v2", "mixtral_8x7b", "deepseek_v3_prefill_fp8"])
-def test_every_gemm_work_item_full_size(name):
-    shape = CONFIGS[name]
-    print("case", name, flush=True)
+# full widths at the workloads' batch sizes, and the DeepSeek-V3 shape at 2048
+# and 4096 tokens, where every routed expert fits one row tile (non-temporal
+# weights: gate/up per item, down per launch) while the shared expert spans
+# several (default policy in gate/up)
+@pytest.mark.parametrize("name,T", [("deepseek_v3_prefill", None), ("deepseek_v2", None), ("mixtral_8x7b", None),
+                                    ("deepseek_v3_prefill_fp8", None), ("deepseek_v3_prefill", 2048),
+                                    ("deepseek_v3_prefill", 4096), ("deepseek_v3_prefill_fp8", 1024)])
+def test_every_gemm_work_item_full_size(name, T):
+    shape = CONFIGS[name] if T is None else CONFIGS[name].with_(T=T)
+    print("case", name, shape.T, flush=True)
     T, E, S, k, H = shape.T, shape.E, shape.S, shape.k, shape.H
     inp = make_inputs(shape, device="cuda")
     cfg = moe.make_config(shape, out_dtype="f32")
