@@ -392,10 +392,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* lds, int e, i
 // expert whose rows fit one row tile are read by that item only and are
 // copied with the non-temporal policy (they stream past the caches), an
 // expert with several row tiles re-reads each weight tile from L2.  NT = 1:
-// every item non-temporal (launches where every expert fits one row tile);
-// NT = 0: the default policy.  (The down GEMM keeps one policy per launch:
-// with both forms of its tile in one kernel its registers spill and it runs
-// slower.)
+// every item non-temporal (down launches whose weight tiles are read once, or
+// mostly once); NT = 0: the default policy.  (The down GEMM keeps one policy
+// per launch: with both forms of its tile in one kernel its registers spill
+// and it runs slower.)
 template <int WM, bool GATEUP, int NT, bool A3>
 __device__ __forceinline__ void gemm_tile_of(const GemmArgs& a, char* lds, const Work& w, int nt) {
   if (NT == 1 || (NT == 2 && w.single))
